@@ -1,0 +1,224 @@
+"""Throughput of the ring-ordered exact attention forward on one MI355X.
+
+A step is one fused ``ra_ring_fwd`` over the whole workload: every ring step
+of the query chunk(s), causal classification and skipping, the online-softmax
+chunk updates, and the final normalization with lse.  Inputs are resident in
+HBM in chunk-major order before timing starts (the layout permutation is the
+data pipeline's job and is not timed).
+
+Default workload: one GPU's share of a 1M-token causal layer, zig-zag layout
+(32 chunks of 32768 tokens; one query chunk of 32 query heads against all 32
+KV chunks of 8 KV heads, d = 128, bf16).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+KERNEL_SOURCE = os.path.join(ROOT, "exact_long_context_amd", "csrc", "attn_fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_zigzag_1m_gqa.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(tasks) -> int:
+    """Visible (query, key) pairs of a schedule, from each task's kind and offset."""
+    tot = 0
+    for t in tasks:
+        if t["kind"] == 0:
+            tot += t["q_len"] * t["kv_len"]
+        elif t["kind"] == 1:
+            p = np.arange(t["q_len"], dtype=np.int64)
+            tot += int(np.clip(p + t["delta"] + 1, 0, t["kv_len"]).sum())
+    return tot
+
+
+def workload_flop(w, ra) -> float:
+    import torch
+    q = torch.empty(1, w.hq, len(w.query_chunks) * w.chunk, w.d, dtype=torch.bfloat16)
+    k = torch.empty(1, w.hkv, w.seq, w.d, dtype=torch.bfloat16)
+    desc = ra.ring_desc(q, k, k, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=w.causal,
+                        q_chunk_first=w.query_chunks[0], q_chunk_count=len(w.query_chunks))
+    pairs = sum(visible_pairs(ra.ra_ring_schedule(desc, i)) for i in w.query_chunks)
+    return 4.0 * w.d * w.hq * w.batch * pairs
+
+
+def time_workload(w, steps, warmup, api, torch):
+    import synthetic
+    q, k, v = synthetic.draw(w, device="cuda")
+    kp = api.to_chunked(k, w.layout, w.n_chunks)
+    vp = api.to_chunked(v, w.layout, w.n_chunks)
+    qp = api.to_chunked(q, w.layout, w.n_chunks) if w.q_chunks is None else q
+    del q, k, v
+    out = torch.empty(qp.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(qp.shape[:3], dtype=torch.float32, device="cuda")
+    from exact_long_context_amd import ringattn as ra
+    desc = ra.ring_desc(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=w.causal,
+                        q_chunk_first=w.query_chunks[0], out=out, lse=lse)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ra.ra_ring_fwd(desc, qp, kp, vp, out, lse, stream=stream)
+    torch.cuda.synchronize()
+    # events on the stream the kernel is launched on
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        ra.ra_ring_fwd(desc, qp, kp, vp, out, lse, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    return ms, wall
+
+
+def cpu_baseline(w, flop_total):
+    """The float64 oracle as it stands, on a bounded sample of the workload's
+    query rows (one KV head's query heads, early and late rows), scaled to the
+    metric's unit by the sample's own FLOP count."""
+    import threadpoolctl
+    import torch
+
+    import synthetic
+    from oracle import attention as OA
+    from oracle import layout as OL
+
+    q, k, v = synthetic.draw(w, device="cuda")
+    G = w.hq // w.hkv
+    rng = np.random.default_rng(2024)
+    L = w.chunk
+    qpos_all = np.concatenate([OL.chunk_positions(w.layout, w.seq, w.n_chunks, c) for c in w.query_chunks])
+    n_rows = 2048
+    rows = np.sort(rng.choice(len(w.query_chunks) * L, size=n_rows, replace=False))
+    heads = rng.integers(0, G, size=n_rows)          # query heads of KV head 0
+    qsel = torch.stack([q[0, int(h), int(r)] for h, r in zip(heads, rows)]).cpu()[None, None]
+    kg = k[:, 0:1].cpu()
+    vg = v[:, 0:1].cpu()
+    del q, k, v
+    torch.cuda.empty_cache()
+    qpos = qpos_all[rows]
+    pairs = int(np.minimum(qpos + 1, w.seq).sum()) if w.causal else n_rows * w.seq
+    flop = 4.0 * w.d * pairs
+    info = threadpoolctl.threadpool_info()
+    threads = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"), default=1)
+    t0 = time.perf_counter()
+    OA.attention_reference(qsel, kg, vg, causal=w.causal, q_pos=qpos, k_pos=np.arange(w.seq))
+    dt = time.perf_counter() - t0
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_rows} query rows of KV head 0 (seeded, both zig-zag segments) against all their "
+                      f"visible keys: {flop:.3e} FLOP in {dt:.2f} s, float64 numpy; the full step would take "
+                      f"{flop_total / (flop / dt) / 3600:.1f} h at this rate"}
+
+
+def traffic_record():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the kernel source as it is now."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    h = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if rec.get("kernel_sha256") != h:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="zigzag_1m_gqa")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run N plain 1 GiB device copies (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the ring runs over KV chunks resident in this GPU's HBM, "
+              f"so --gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic
+    from exact_long_context_amd import api
+    from exact_long_context_amd import ringattn as ra
+
+    if args.copy_calib:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(args.copy_calib):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 2, "copy_bytes_written": b.numel() * 2,
+                          "copies": args.copy_calib}))
+        return
+
+    w = synthetic.WORKLOADS[args.workload]
+    flop = workload_flop(w, ra)
+    log(f"workload {w.name}: {flop:.4e} FLOP per step (causal-adjusted)")
+    ms, wall = time_workload(w, args.steps, args.warmup, api, torch)
+    tflops = flop / (ms * 1e-3) / 1e12
+    log(f"  {ms:.3f} ms/step  {tflops:.1f} TFLOP/s  ({tflops / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 peak)")
+
+    others = {}
+    if not args.no_others:
+        for name in ("mha_8k", "mha_8k_sharp", "causal_contig_32k", "causal_striped_128k"):
+            wo = synthetic.WORKLOADS[name]
+            fo = workload_flop(wo, ra)
+            mo, _ = time_workload(wo, max(3, args.steps), 2, api, torch)
+            others[name] = {"ms": round(mo, 4), "tflops": round(fo / (mo * 1e-3) / 1e12, 2)}
+            log(f"  {name}: {mo:.3f} ms  {others[name]['tflops']} TFLOP/s")
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the float64 oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, flop)
+        log(f"  cpu oracle {cpu['value']} TFLOP/s on {cpu['cores']} threads")
+
+    achieved = tflops  # one launch per step: algorithmic FLOP per launch / mean launch time
+    res = {
+        "metric": "ring-chunked attention fwd TFLOP/s (causal-adjusted), % of bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: one query chunk of a {w.seq}-token causal layer, {w.layout} layout, "
+                               f"{w.n_chunks} chunks of {w.chunk}, {w.hq} query / {w.hkv} KV heads, d={w.d}, "
+                               f"all KV chunks resident in HBM",
+                   "global_batch": w.batch, "seq_len": w.seq, "parallelism": "none (one GPU's share)",
+                   "flop_per_step": flop, "pct_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS * 100, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_record()},
+        "cpu_baseline": cpu,
+        "other_workloads": others,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,93 @@
+"""Tensor-level helpers over the C ABI: allocate outputs with torch, build the
+descriptors, call the library.  No arithmetic happens here."""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import ringattn as ra
+
+
+def to_chunked(x: torch.Tensor, layout: str, n_chunks: int, stream=None) -> torch.Tensor:
+    """Logical token order [B, H, S, d] -> chunk-major physical order."""
+    x = x.contiguous()
+    out = torch.empty_like(x)
+    ra.ra_permute(layout, True, x, out, n_chunks, stream)
+    return out
+
+
+def from_chunked(x: torch.Tensor, layout: str, n_chunks: int, stream=None) -> torch.Tensor:
+    """Chunk-major physical order -> logical token order."""
+    x = x.contiguous()
+    out = torch.empty_like(x)
+    ra.ra_permute(layout, False, x, out, n_chunks, stream)
+    return out
+
+
+def ring_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, seq: int, n_chunks: int, layout: str,
+                 causal: bool, q_chunk_first: int = 0, out_dtype: Optional[torch.dtype] = None,
+                 return_lse: bool = True, scale: float = 0.0, stream=None):
+    """All ring steps for the query chunks held in ``q`` (physical order).
+
+    q: [B, Hq, n_q * L, d]; k, v: [B, Hkv, seq, d] in chunk-major order.
+    Returns (out [B, Hq, n_q * L, d], lse [B, Hq, n_q * L] fp32 or None)."""
+    B, Hq, rows, d = q.shape
+    out = torch.empty(B, Hq, rows, d, dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty(B, Hq, rows, dtype=torch.float32, device=q.device) if return_lse else None
+    desc = ra.ring_desc(q, k, v, seq=seq, n_chunks=n_chunks, layout=layout, causal=causal,
+                        q_chunk_first=q_chunk_first, out=out, lse=lse, scale=scale)
+    ra.ra_ring_fwd(desc, q, k, v, out, lse, stream=stream)
+    return out, lse
+
+
+class ChunkState:
+    """Running (m, l, o) of a query block, fp32, contiguous."""
+
+    def __init__(self, q: torch.Tensor):
+        B, Hq, Lq, d = q.shape
+        self.m = torch.empty(B, Hq, Lq, dtype=torch.float32, device=q.device)
+        self.l = torch.empty_like(self.m)
+        self.o = torch.empty(B, Hq, Lq, d, dtype=torch.float32, device=q.device)
+
+
+def state_init(q: torch.Tensor, k: torch.Tensor, stream=None) -> ChunkState:
+    st = ChunkState(q)
+    desc = ra.attn_desc(q, k, k, ml=st.m, o=st.o)
+    ra.ra_state_init(desc, st.m, st.l, st.o, stream)
+    return st
+
+
+def chunk_forward(st: ChunkState, q, k, v, *, causal: bool = False, delta: int = 0, scale: float = 0.0,
+                  stream=None) -> ChunkState:
+    desc = ra.attn_desc(q, k, v, ml=st.m, o=st.o, scale=scale)
+    ra.ra_chunk_fwd(desc, q, k, v, st.m, st.l, st.o, delta, causal, stream)
+    return st
+
+
+def finalize(st: ChunkState, q, out_dtype: Optional[torch.dtype] = None, stream=None):
+    B, Hq, Lq, d = q.shape
+    out = torch.empty(B, Hq, Lq, d, dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device=q.device)
+    desc = ra.attn_desc(q, q, q, out=out, ml=st.m, o=st.o)
+    ra.ra_finalize(desc, st.m, st.l, st.o, out, lse, stream)
+    return out, lse
+
+
+def merge(lse_a, o_a, lse_b, o_b, lse_out=None, o_out=None, stream=None):
+    """Log-sum-exp merge of two normalized fp32 partials [B, H, L] / [B, H, L, d]."""
+    lse_out = torch.empty_like(lse_a) if lse_out is None else lse_out
+    o_out = torch.empty_like(o_a) if o_out is None else o_out
+    B, H, L, d = o_a.shape
+    desc = ra.ra_attn_desc()
+    desc.batch, desc.hq, desc.hkv, desc.lq, desc.lk, desc.d = B, H, H, L, L, d
+    desc.in_dtype = desc.out_dtype = ra.RA_F32
+    desc.q = desc.k = desc.v = desc.out = ra.ra_strides(H * L * d, L * d, d)
+    desc.ml = ra.ra_strides(lse_a.stride(0), lse_a.stride(1), 1)
+    desc.o = ra.strides_of(o_a)
+    for t in (lse_b, lse_out):
+        assert t.stride() == lse_a.stride()
+    for t in (o_b, o_out):
+        assert t.stride() == o_a.stride()
+    ra.ra_merge(desc, lse_a, o_a, lse_b, o_b, lse_out, o_out, stream)
+    return lse_out, o_out

@@ -1,0 +1,182 @@
+// Memory-bound kernels of the library: state initialization, finalize, the
+// log-sum-exp merge of two partials, and the layout permutation.
+//
+// Row kernels give each row to a group of d/4 consecutive lanes, each lane
+// moving 16 bytes of the row, so a wave touches 64 consecutive 16-byte pieces
+// of the row-major tensors (coalesced) and reads every per-row scalar once per
+// lane group, before any lane of that group writes (which makes the in-place
+// merge safe).
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+#include "schedule.h"
+
+namespace ra {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int ROW_THREADS = 256;
+
+struct RowIdx {
+  bool ok;
+  int64_t ml;   // index into m / l / lse
+  int64_t o;    // index of this lane's 4 floats in o
+  int64_t out;  // index of this lane's 4 elements in out
+  int c4;       // which 4-element piece
+};
+
+__device__ __forceinline__ RowIdx row_index(const RowsArgs& g) {
+  const int lpr = g.d >> 2;  // lanes per row
+  const int64_t t = (int64_t)blockIdx.x * ROW_THREADS + threadIdx.x;
+  const int64_t row = t / lpr;
+  RowIdx r;
+  r.c4 = (int)(t - row * lpr);
+  const int64_t total = (int64_t)g.batch * g.heads * g.rows;
+  r.ok = row < total;
+  const int64_t bh = row / g.rows;
+  const int64_t p = row - bh * g.rows;
+  const int64_t b = bh / g.heads, h = bh - b * g.heads;
+  r.ml = b * g.ml_sb + h * g.ml_sh + p;
+  r.o = b * g.o_sb + h * g.o_sh + p * g.o_ss + 4 * r.c4;
+  r.out = b * g.out_sb + h * g.out_sh + p * g.out_ss + 4 * r.c4;
+  return r;
+}
+
+__global__ __launch_bounds__(ROW_THREADS) void state_init_kernel(RowsArgs g, float* m, float* l, float* o) {
+  const RowIdx r = row_index(g);
+  if (!r.ok) return;
+  if (r.c4 == 0) {
+    m[r.ml] = -INFINITY;
+    l[r.ml] = 0.f;
+  }
+  *(f32x4*)(o + r.o) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+__global__ __launch_bounds__(ROW_THREADS) void finalize_kernel(RowsArgs g, const float* m, const float* l,
+                                                               const float* o, void* out, int out_bf16,
+                                                               float* lse) {
+  const RowIdx r = row_index(g);
+  if (!r.ok) return;
+  const float lv = l[r.ml];
+  const bool seen = lv > 0.f;
+  const float inv = seen ? 1.f / lv : 0.f;
+  const f32x4 v = *(const f32x4*)(o + r.o) * inv;
+  if (out_bf16) {
+    bf16x4 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = (__bf16)v[e];
+    *(bf16x4*)((__bf16*)out + r.out) = b;
+  } else {
+    *(f32x4*)((float*)out + r.out) = v;
+  }
+  if (lse != nullptr && r.c4 == 0) lse[r.ml] = seen ? m[r.ml] + logf(lv) : -INFINITY;
+}
+
+__global__ __launch_bounds__(ROW_THREADS) void merge_kernel(RowsArgs g, const float* lse_a, const float* o_a,
+                                                            const float* lse_b, const float* o_b, float* lse_out,
+                                                            float* o_out) {
+  const RowIdx r = row_index(g);
+  if (!r.ok) return;
+  const float la = lse_a[r.ml], lb = lse_b[r.ml];
+  const f32x4 va = *(const f32x4*)(o_a + r.o);
+  const f32x4 vb = *(const f32x4*)(o_b + r.o);
+  const float M = fmaxf(la, lb);
+  float lse, wa, wb;
+  if (M == -INFINITY) {
+    lse = -INFINITY; wa = 0.f; wb = 0.f;
+  } else {
+    const float ea = expf(la - M), eb = expf(lb - M);  // exp(-inf) = 0
+    const float tot = ea + eb;
+    lse = M + logf(tot);
+    wa = ea / tot;
+    wb = eb / tot;
+  }
+  *(f32x4*)(o_out + r.o) = va * wa + vb * wb;
+  if (r.c4 == 0) lse_out[r.ml] = lse;
+}
+
+// Permutation: physical row c*L + p  <->  logical row pos(c, p).  Each thread
+// moves one UNIT-byte piece.
+template <typename UNIT>
+__global__ __launch_bounds__(256) void permute_kernel(int32_t layout, int32_t to_chunked, int64_t bh_count,
+                                                      int64_t seq, int32_t n, int64_t units_per_row,
+                                                      const UNIT* __restrict__ src, UNIT* __restrict__ dst) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = bh_count * seq * units_per_row;
+  if (t >= total) return;
+  const int64_t row = t / units_per_row;
+  const int64_t u = t - row * units_per_row;
+  const int64_t bh = row / seq;
+  const int64_t phys = row - bh * seq;
+  const int64_t L = seq / n;
+  const int32_t c = (int32_t)(phys / L);
+  const int64_t logical = position(layout, seq, n, c, phys - (int64_t)c * L);
+  const int64_t base = bh * seq;
+  if (to_chunked) dst[(base + phys) * units_per_row + u] = src[(base + logical) * units_per_row + u];
+  else dst[(base + logical) * units_per_row + u] = src[(base + phys) * units_per_row + u];
+}
+
+inline unsigned blocks_for(int64_t threads, int per) { return (unsigned)((threads + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_state_init(const RowsArgs& g, float* m, float* l, float* o, hipStream_t stream) {
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(state_init_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g, m,
+                     l, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const RowsArgs& g, const float* m, const float* l, const float* o, void* out,
+                           int32_t out_bf16, float* lse, hipStream_t stream) {
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g, m,
+                     l, o, out, out_bf16, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const RowsArgs& g, const float* lse_a, const float* o_a, const float* lse_b,
+                        const float* o_b, float* lse_out, float* o_out, hipStream_t stream) {
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g, lse_a,
+                     o_a, lse_b, o_b, lse_out, o_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(int32_t layout, int32_t to_chunked, int64_t batch_heads, int64_t seq, int32_t n_chunks,
+                          int64_t row_bytes, int unit, const void* src, void* dst, hipStream_t stream) {
+  const int64_t upr = row_bytes / unit;
+  const int64_t threads = batch_heads * seq * upr;
+  if (threads == 0) return hipSuccess;
+  const dim3 grid(blocks_for(threads, 256)), block(256);
+  switch (unit) {
+    case 16:
+      hipLaunchKernelGGL(permute_kernel<uint4>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
+                         n_chunks, upr, (const uint4*)src, (uint4*)dst);
+      break;
+    case 8:
+      hipLaunchKernelGGL(permute_kernel<uint2>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
+                         n_chunks, upr, (const uint2*)src, (uint2*)dst);
+      break;
+    case 4:
+      hipLaunchKernelGGL(permute_kernel<uint32_t>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
+                         n_chunks, upr, (const uint32_t*)src, (uint32_t*)dst);
+      break;
+    case 2:
+      hipLaunchKernelGGL(permute_kernel<uint16_t>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
+                         n_chunks, upr, (const uint16_t*)src, (uint16_t*)dst);
+      break;
+    default:
+      hipLaunchKernelGGL(permute_kernel<uint8_t>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
+                         n_chunks, upr, (const uint8_t*)src, (uint8_t*)dst);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

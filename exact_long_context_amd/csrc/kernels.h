@@ -1,0 +1,72 @@
+// Internal interface between the C ABI (ringattn_abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Arguments of the fused attention-forward kernels.  One launch covers either
+// a single chunk update with the running state in HBM (mode CHUNK) or the
+// whole ring for a range of query chunks with the state kept on chip and the
+// output finalized at the end (mode RING).
+enum FwdMode : int32_t { MODE_CHUNK = 0, MODE_RING = 1 };
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  // running state (MODE_CHUNK): m, l [B, Hq, Lq]; o [B, Hq, Lq, d]
+  float* m;
+  float* l;
+  float* o;
+  int64_t ml_sb, ml_sh;
+  int64_t o_sb, o_sh, o_ss;
+  // normalized output and lse (MODE_RING); lse may be null
+  void* out;
+  int64_t out_sb, out_sh, out_ss;
+  float* lse;
+  int32_t out_bf16;
+  int32_t batch, hq, hkv, d;
+  int32_t mode;
+  int32_t causal;
+  // ring geometry (MODE_RING): chunk length L, layout, N chunks
+  int32_t layout;
+  int32_t n_chunks;
+  int64_t seq;
+  int32_t q_first, q_count;
+  // chunk geometry (MODE_CHUNK): lq query rows, lk key rows, one offset
+  int32_t lq, lk;
+  int64_t delta;
+  float scale_log2;  // scale * log2(e)
+  // work decomposition, filled by the host planner
+  int32_t heads_per_wg;   // query heads of one KV head handled by one workgroup
+  int32_t rows_per_wg;    // query rows of one segment handled by one workgroup
+  int32_t nseg_q;         // query segments per query chunk (2 for zig-zag)
+  int32_t tiles_per_seg;  // workgroups along one query segment
+  int32_t xcd_swizzle;    // map workgroups so that one KV stream stays on one XCD
+  int32_t n_work;         // total workgroups
+};
+
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+struct RowsArgs {  // [B, H, rows] fp32 tensors with strides (b, h), row stride 1; o-like with (b, h, s)
+  int32_t batch, heads, rows, d;
+  int64_t ml_sb, ml_sh;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t out_sb, out_sh, out_ss;
+};
+
+hipError_t launch_state_init(const RowsArgs& g, float* m, float* l, float* o, hipStream_t stream);
+hipError_t launch_finalize(const RowsArgs& g, const float* m, const float* l, const float* o, void* out,
+                           int32_t out_bf16, float* lse, hipStream_t stream);
+hipError_t launch_merge(const RowsArgs& g, const float* lse_a, const float* o_a, const float* lse_b,
+                        const float* o_b, float* lse_out, float* o_out, hipStream_t stream);
+hipError_t launch_permute(int32_t layout, int32_t to_chunked, int64_t batch_heads, int64_t seq, int32_t n_chunks,
+                          int64_t row_bytes, int unit, const void* src, void* dst, hipStream_t stream);
+
+}  // namespace ra

@@ -1,0 +1,342 @@
+// The C ABI of libringattn: argument validation (on the host, before any HIP
+// call), the host-side schedule and layout queries, and the launch planning
+// of the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ringattn.h"
+#include "kernels.h"
+#include "schedule.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ra_status fail(ra_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ra_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RA_OK;
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t I32_MAX = 2147483647;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int32_t dt) { return dt == RA_BF16 ? 2 : 4; }
+
+ra_status check_strides(const char* name, const ra_strides& s, int32_t dtype) {
+  const int64_t unit = 16 / elem_bytes(dtype);
+  if (s.b < 0 || s.h < 0 || s.s < 0) return fail(RA_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (s.b % unit || s.h % unit || s.s % unit)
+    return fail(RA_ERR_INVALID_ARG, "%s: strides must be multiples of %lld elements", name, (long long)unit);
+  return RA_OK;
+}
+
+// Shape, dtype and stride checks common to every entry point that takes an
+// attention descriptor.
+ra_status check_attn(const ra_attn_desc* d) {
+  if (d == nullptr) return fail(RA_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->reserved != 0) return fail(RA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (d->batch < 1 || d->hq < 1 || d->hkv < 1 || d->lq < 1 || d->lk < 1 || d->d < 1)
+    return fail(RA_ERR_INVALID_ARG, "batch, heads, rows and d must be >= 1");
+  if (d->hq % d->hkv) return fail(RA_ERR_INVALID_ARG, "hq (%lld) is not a multiple of hkv (%lld)",
+                                  (long long)d->hq, (long long)d->hkv);
+  if (d->lq > I32_MAX || d->lk > I32_MAX || d->batch * d->hq > I32_MAX)
+    return fail(RA_ERR_INVALID_ARG, "rows or batch*heads exceed 2^31-1");
+  if (d->in_dtype != RA_F32 && d->in_dtype != RA_BF16) return fail(RA_ERR_INVALID_ARG, "unknown in_dtype");
+  if (d->out_dtype != RA_F32 && d->out_dtype != RA_BF16) return fail(RA_ERR_INVALID_ARG, "unknown out_dtype");
+  if (!(d->scale <= 0.f || std::isfinite(d->scale))) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  if (d->in_dtype == RA_BF16 && d->d != 128)
+    return fail(RA_ERR_UNSUPPORTED, "bf16 inputs need d = 128 (got %lld)", (long long)d->d);
+  if (d->in_dtype == RA_F32 && d->d != 16 && d->d != 32 && d->d != 64 && d->d != 128)
+    return fail(RA_ERR_UNSUPPORTED, "fp32 inputs need d in {16, 32, 64, 128} (got %lld)", (long long)d->d);
+  ra_status st;
+  if ((st = check_strides("q", d->q, d->in_dtype)) != RA_OK) return st;
+  if ((st = check_strides("k", d->k, d->in_dtype)) != RA_OK) return st;
+  if ((st = check_strides("v", d->v, d->in_dtype)) != RA_OK) return st;
+  if ((st = check_strides("out", d->out, d->out_dtype)) != RA_OK) return st;
+  if ((st = check_strides("o", d->o, RA_F32)) != RA_OK) return st;
+  if (d->ml.s != 1) return fail(RA_ERR_INVALID_ARG, "ml.s must be 1");
+  if (d->ml.b < 0 || d->ml.h < 0) return fail(RA_ERR_INVALID_ARG, "ml: negative stride");
+  return RA_OK;
+}
+
+// The row kernels give every row d/4 lanes; d is one of 16..128 here.
+ra::RowsArgs rows_args(const ra_attn_desc* d) {
+  ra::RowsArgs g;
+  g.batch = (int32_t)d->batch;
+  g.heads = (int32_t)d->hq;
+  g.rows = (int32_t)d->lq;
+  g.d = (int32_t)d->d;
+  g.ml_sb = d->ml.b; g.ml_sh = d->ml.h;
+  g.o_sb = d->o.b; g.o_sh = d->o.h; g.o_ss = d->o.s;
+  g.out_sb = d->out.b; g.out_sh = d->out.h; g.out_ss = d->out.s;
+  return g;
+}
+
+float log2_scale(const ra_attn_desc* d) {
+  const double sc = d->scale > 0.f ? (double)d->scale : 1.0 / std::sqrt((double)d->d);
+  return (float)(sc * 1.4426950408889634074);
+}
+
+void fill_common(ra::FwdArgs& a, const ra_attn_desc* d, const void* q, const void* k, const void* v) {
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v;
+  a.q_sb = d->q.b; a.q_sh = d->q.h; a.q_ss = d->q.s;
+  a.k_sb = d->k.b; a.k_sh = d->k.h; a.k_ss = d->k.s;
+  a.v_sb = d->v.b; a.v_sh = d->v.h; a.v_ss = d->v.s;
+  a.ml_sb = d->ml.b; a.ml_sh = d->ml.h;
+  a.o_sb = d->o.b; a.o_sh = d->o.h; a.o_ss = d->o.s;
+  a.out_sb = d->out.b; a.out_sh = d->out.h; a.out_ss = d->out.s;
+  a.out_bf16 = d->out_dtype == RA_BF16;
+  a.batch = (int32_t)d->batch;
+  a.hq = (int32_t)d->hq;
+  a.hkv = (int32_t)d->hkv;
+  a.d = (int32_t)d->d;
+  a.scale_log2 = log2_scale(d);
+}
+
+// Work decomposition.  bf16: 4 waves of 64 rows per workgroup; the waves are
+// query heads of one KV head when the group size allows (GQA shares every K/V
+// tile over the heads), else consecutive row blocks of one head.  fp32: one
+// wave of 64 rows.
+ra_status plan_launch(ra::FwdArgs& a, bool bf16, int64_t seg_len, int32_t nseg_q, int32_t q_count) {
+  const int32_t G = a.hq / a.hkv;
+  if (bf16) {
+    a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+    a.rows_per_wg = 64 * 4 / a.heads_per_wg;
+  } else {
+    a.heads_per_wg = 1;
+    a.rows_per_wg = 64;
+  }
+  a.nseg_q = nseg_q;
+  const int64_t tps = (seg_len + a.rows_per_wg - 1) / a.rows_per_wg;
+  const int64_t streams = (int64_t)a.batch * a.hkv;
+  const int64_t total = streams * (G / a.heads_per_wg) * q_count * nseg_q * tps;
+  if (tps > I32_MAX || total > I32_MAX) return fail(RA_ERR_INVALID_ARG, "problem too large for one launch");
+  a.tiles_per_seg = (int32_t)tps;
+  a.n_work = (int32_t)total;
+  a.xcd_swizzle = (streams % 8 == 0) ? 1 : 0;
+  return RA_OK;
+}
+
+ra_status check_ring(const ra_ring_desc* r) {
+  if (r == nullptr) return fail(RA_ERR_INVALID_ARG, "ring descriptor is NULL");
+  if (r->reserved != 0) return fail(RA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (r->n_chunks < 1 || r->seq < 1) return fail(RA_ERR_INVALID_ARG, "seq and n_chunks must be >= 1");
+  if (r->seq % r->n_chunks) return fail(RA_ERR_INVALID_ARG, "seq (%lld) is not a multiple of n_chunks (%d)",
+                                        (long long)r->seq, r->n_chunks);
+  if (r->layout != RA_LAYOUT_CONTIGUOUS && r->layout != RA_LAYOUT_STRIPED && r->layout != RA_LAYOUT_ZIGZAG)
+    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", r->layout);
+  const int64_t L = r->seq / r->n_chunks;
+  if (r->layout == RA_LAYOUT_ZIGZAG && (L % 2)) return fail(RA_ERR_INVALID_ARG, "zig-zag needs an even chunk length");
+  if (r->causal != 0 && r->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (r->q_chunk_first < 0 || r->q_chunk_count < 1 || (int64_t)r->q_chunk_first + r->q_chunk_count > r->n_chunks)
+    return fail(RA_ERR_INVALID_ARG, "query chunk range out of [0, n_chunks)");
+  if (r->attn.lq != L || r->attn.lk != L)
+    return fail(RA_ERR_INVALID_ARG, "attn.lq and attn.lk must equal seq / n_chunks (%lld)", (long long)L);
+  if (r->seq > I32_MAX) return fail(RA_ERR_INVALID_ARG, "seq exceeds 2^31-1");
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_abi_version(void) { return RA_ABI_VERSION; }
+
+const char* ra_status_str(ra_status s) {
+  switch (s) {
+    case RA_OK: return "ok";
+    case RA_ERR_INVALID_ARG: return "invalid argument";
+    case RA_ERR_UNSUPPORTED: return "unsupported";
+    case RA_ERR_WORKSPACE: return "workspace too small";
+    case RA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ra_last_error(void) { return g_err; }
+
+ra_status ra_state_init(const ra_attn_desc* desc, float* m, float* l, float* o, ra_stream stream) {
+  ra_status st = check_attn(desc);
+  if (st != RA_OK) return st;
+  if (!m || !l || !o) return fail(RA_ERR_INVALID_ARG, "m, l and o must be non-NULL");
+  if (!aligned16(o)) return fail(RA_ERR_INVALID_ARG, "o must be 16-byte aligned");
+  return hip_status(ra::launch_state_init(rows_args(desc), m, l, o, (hipStream_t)stream), "ra_state_init");
+}
+
+ra_status ra_chunk_fwd(const ra_attn_desc* desc, const void* q, const void* k, const void* v, float* m, float* l,
+                       float* o, int64_t causal_delta, int32_t causal, ra_stream stream) {
+  ra_status st = check_attn(desc);
+  if (st != RA_OK) return st;
+  if (!q || !k || !v || !m || !l || !o) return fail(RA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(RA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (causal != 0 && causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  ra::FwdArgs a;
+  fill_common(a, desc, q, k, v);
+  a.m = m; a.l = l; a.o = o;
+  a.mode = ra::MODE_CHUNK;
+  a.causal = causal;
+  a.lq = (int32_t)desc->lq;
+  a.lk = (int32_t)desc->lk;
+  a.delta = causal ? causal_delta : 0;
+  a.n_chunks = 1;
+  a.q_count = 1;
+  const bool bf16 = desc->in_dtype == RA_BF16;
+  if ((st = plan_launch(a, bf16, desc->lq, 1, 1)) != RA_OK) return st;
+  // a causal offset below -(lq - 1) hides every key: nothing to do
+  if (causal && causal_delta < -(desc->lq - 1)) return RA_OK;
+  return hip_status(bf16 ? ra::launch_attn_fwd_bf16(a, (hipStream_t)stream)
+                         : ra::launch_attn_fwd_f32(a, (hipStream_t)stream),
+                    "ra_chunk_fwd");
+}
+
+ra_status ra_finalize(const ra_attn_desc* desc, const float* m, const float* l, const float* o, void* out,
+                      float* lse, ra_stream stream) {
+  ra_status st = check_attn(desc);
+  if (st != RA_OK) return st;
+  if (!m || !l || !o || !out) return fail(RA_ERR_INVALID_ARG, "m, l, o and out must be non-NULL");
+  if (!aligned16(o) || !aligned16(out)) return fail(RA_ERR_INVALID_ARG, "o and out must be 16-byte aligned");
+  return hip_status(ra::launch_finalize(rows_args(desc), m, l, o, out, desc->out_dtype == RA_BF16, lse,
+                                        (hipStream_t)stream),
+                    "ra_finalize");
+}
+
+ra_status ra_merge(const ra_attn_desc* desc, const float* lse_a, const float* o_a, const float* lse_b,
+                   const float* o_b, float* lse_out, float* o_out, ra_stream stream) {
+  ra_status st = check_attn(desc);
+  if (st != RA_OK) return st;
+  if (!lse_a || !o_a || !lse_b || !o_b || !lse_out || !o_out)
+    return fail(RA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out))
+    return fail(RA_ERR_INVALID_ARG, "o tensors must be 16-byte aligned");
+  return hip_status(ra::launch_merge(rows_args(desc), lse_a, o_a, lse_b, o_b, lse_out, o_out, (hipStream_t)stream),
+                    "ra_merge");
+}
+
+size_t ra_ring_workspace_bytes(const ra_ring_desc* desc) {
+  (void)desc;
+  return 0;
+}
+
+ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, ra_stream stream) {
+  ra_status st = check_ring(desc);
+  if (st != RA_OK) return st;
+  if ((st = check_attn(&desc->attn)) != RA_OK) return st;
+  if (!q || !k || !v || !out) return fail(RA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(RA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (workspace_bytes < ra_ring_workspace_bytes(desc)) return fail(RA_ERR_WORKSPACE, "workspace too small");
+  (void)workspace;
+  const ra_attn_desc* d = &desc->attn;
+  ra::FwdArgs a;
+  fill_common(a, d, q, k, v);
+  a.out = out;
+  a.lse = lse;
+  a.mode = ra::MODE_RING;
+  a.causal = desc->causal;
+  a.layout = desc->layout;
+  a.n_chunks = desc->n_chunks;
+  a.seq = desc->seq;
+  a.q_first = desc->q_chunk_first;
+  a.q_count = desc->q_chunk_count;
+  a.lq = (int32_t)d->lq;
+  a.lk = (int32_t)d->lk;
+  const int32_t nseg = ra::num_segments(desc->layout);
+  const bool bf16 = d->in_dtype == RA_BF16;
+  if ((st = plan_launch(a, bf16, d->lq / nseg, nseg, desc->q_chunk_count)) != RA_OK) return st;
+  return hip_status(bf16 ? ra::launch_attn_fwd_bf16(a, (hipStream_t)stream)
+                         : ra::launch_attn_fwd_f32(a, (hipStream_t)stream),
+                    "ra_ring_fwd");
+}
+
+ra_status ra_layout_positions(int32_t layout, int64_t seq, int32_t n_chunks, int32_t chunk, int64_t* pos) {
+  if (pos == nullptr) return fail(RA_ERR_INVALID_ARG, "pos is NULL");
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED && layout != RA_LAYOUT_ZIGZAG)
+    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  if (n_chunks < 1 || seq < 1 || seq % n_chunks) return fail(RA_ERR_INVALID_ARG, "seq must be a multiple of n_chunks");
+  const int64_t L = seq / n_chunks;
+  if (layout == RA_LAYOUT_ZIGZAG && (L % 2)) return fail(RA_ERR_INVALID_ARG, "zig-zag needs an even chunk length");
+  if (chunk < 0 || chunk >= n_chunks) return fail(RA_ERR_INVALID_ARG, "chunk out of range");
+  for (int64_t p = 0; p < L; ++p) pos[p] = ra::position(layout, seq, n_chunks, chunk, p);
+  return RA_OK;
+}
+
+ra_status ra_ring_schedule(const ra_ring_desc* desc, int32_t q_chunk, ra_task* tasks, int32_t capacity,
+                           int32_t* n_tasks) {
+  ra_status st = check_ring(desc);
+  if (st != RA_OK) return st;
+  if (n_tasks == nullptr) return fail(RA_ERR_INVALID_ARG, "n_tasks is NULL");
+  if (q_chunk < 0 || q_chunk >= desc->n_chunks) return fail(RA_ERR_INVALID_ARG, "q_chunk out of range");
+  const int32_t n = desc->n_chunks;
+  const int32_t nseg = ra::num_segments(desc->layout);
+  const int64_t count = (int64_t)n * nseg * nseg;
+  if (count > I32_MAX) return fail(RA_ERR_INVALID_ARG, "schedule too long");
+  *n_tasks = (int32_t)count;
+  if (capacity < count || (count > 0 && tasks == nullptr))
+    return fail(RA_ERR_INVALID_ARG, "capacity %d < %lld tasks", capacity, (long long)count);
+  int32_t idx = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    const int32_t j = ra::ring_kv_chunk(q_chunk, t, n);
+    for (int qs = 0; qs < nseg; ++qs) {
+      const ra::Segment qseg = ra::segment(desc->layout, desc->seq, n, q_chunk, qs);
+      for (int ks = 0; ks < nseg; ++ks) {
+        const ra::Segment kseg = ra::segment(desc->layout, desc->seq, n, j, ks);
+        ra_task& e = tasks[idx++];
+        e.step = t;
+        e.kv_chunk = j;
+        e.q_row0 = qseg.row0;
+        e.q_len = qseg.len;
+        e.kv_row0 = kseg.row0;
+        e.kv_len = kseg.len;
+        e.reserved = 0;
+        if (desc->causal) {
+          e.delta = ra::pair_delta(qseg, kseg);
+          e.kind = ra::pair_kind(e.delta, qseg.len, kseg.len);
+        } else {
+          e.delta = 0;
+          e.kind = RA_FULL;
+        }
+      }
+    }
+  }
+  return RA_OK;
+}
+
+ra_status ra_permute(int32_t layout, int32_t to_chunked, int64_t batch, int64_t heads, int64_t seq,
+                     int32_t n_chunks, int64_t d, int32_t dtype, const void* src, void* dst, ra_stream stream) {
+  if (!src || !dst) return fail(RA_ERR_INVALID_ARG, "src and dst must be non-NULL");
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED && layout != RA_LAYOUT_ZIGZAG)
+    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 1 || heads < 1 || d < 1 || n_chunks < 1 || seq < 1 || seq % n_chunks)
+    return fail(RA_ERR_INVALID_ARG, "bad shape");
+  if (layout == RA_LAYOUT_ZIGZAG && ((seq / n_chunks) % 2))
+    return fail(RA_ERR_INVALID_ARG, "zig-zag needs an even chunk length");
+  if (to_chunked != 0 && to_chunked != 1) return fail(RA_ERR_INVALID_ARG, "to_chunked must be 0 or 1");
+  const int64_t row_bytes = d * elem_bytes(dtype);
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
+  if (addr % elem_bytes(dtype)) return fail(RA_ERR_INVALID_ARG, "misaligned pointer");
+  // widest piece (16, 8, 4 or 2 bytes) that divides the row and both pointers
+  int unit = 16;
+  while ((row_bytes % unit) || (addr % unit)) unit >>= 1;
+  return hip_status(ra::launch_permute(layout, to_chunked, batch * heads, seq, n_chunks, row_bytes, unit, src, dst,
+                                       (hipStream_t)stream),
+                    "ra_permute");
+}
+
+}  // extern "C"

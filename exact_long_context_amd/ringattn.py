@@ -1,0 +1,250 @@
+"""ctypes binding of libringattn (argument marshalling only).
+
+Every entry point of ``include/ringattn.h`` has a Python function of the same
+name.  Tensors are torch tensors on the GPU (PyTorch supplies device memory and
+streams; all arithmetic runs in the library's HIP kernels).  A non-OK status
+raises :class:`RingAttnError` carrying the library's message.
+
+If the shared library has not been built, importing this module raises
+ImportError: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libringattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with `python -m exact_long_context_amd.build` "
+                      "(or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---- enums (mirror include/ringattn.h)
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(5)
+RA_F32, RA_BF16 = 0, 1
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
+RA_FULL, RA_MASKED, RA_SKIP = 0, 1, 2
+LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED, "zigzag": RA_LAYOUT_ZIGZAG}
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.ra_last_error().decode()
+        super().__init__(f"{where}: {_lib.ra_status_str(status).decode()} ({msg})")
+
+
+class ra_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("s", ctypes.c_int64)]
+
+
+class ra_attn_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("hq", ctypes.c_int64), ("hkv", ctypes.c_int64),
+                ("lq", ctypes.c_int64), ("lk", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("q", ra_strides), ("k", ra_strides), ("v", ra_strides), ("out", ra_strides),
+                ("ml", ra_strides), ("o", ra_strides),
+                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+class ra_ring_desc(ctypes.Structure):
+    _fields_ = [("attn", ra_attn_desc), ("seq", ctypes.c_int64), ("n_chunks", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("causal", ctypes.c_int32), ("q_chunk_first", ctypes.c_int32),
+                ("q_chunk_count", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ra_task(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("kv_chunk", ctypes.c_int32), ("q_row0", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("kv_row0", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("delta", ctypes.c_int64), ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_P = ctypes.POINTER
+_sigs = {
+    "ra_abi_version": (ctypes.c_int, []),
+    "ra_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "ra_last_error": (ctypes.c_char_p, []),
+    "ra_state_init": (ctypes.c_int, [_P(ra_attn_desc), _vp, _vp, _vp, _vp]),
+    "ra_chunk_fwd": (ctypes.c_int, [_P(ra_attn_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                    ctypes.c_int32, _vp]),
+    "ra_finalize": (ctypes.c_int, [_P(ra_attn_desc), _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ra_merge": (ctypes.c_int, [_P(ra_attn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ra_ring_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
+    "ra_ring_fwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ra_layout_positions": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           _P(ctypes.c_int64)]),
+    "ra_ring_schedule": (ctypes.c_int, [_P(ra_ring_desc), ctypes.c_int32, _P(ra_task), ctypes.c_int32,
+                                        _P(ctypes.c_int32)]),
+    "ra_permute": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
+}
+for _name, (_res, _args) in _sigs.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_sigs)
+
+
+def _check(st: int, where: str):
+    if st != RA_OK:
+        raise RingAttnError(st, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def strides_of(t) -> ra_strides:
+    """(b, h, s) element strides of a [B, H, S, ...] tensor."""
+    st = t.stride()
+    return ra_strides(st[0], st[1], st[2])
+
+
+def attn_desc(q, k, v, *, out=None, ml=None, o=None, out_dtype=None, scale: float = 0.0,
+              lq: Optional[int] = None, lk: Optional[int] = None) -> ra_attn_desc:
+    """Descriptor from tensors: q [B, Hq, Lq, d], k/v [B, Hkv, Lk, d]; ``out``
+    (or ``out_dtype``), ``ml`` ([B, Hq, Lq] fp32) and ``o`` ([B, Hq, Lq, d] fp32)
+    supply the remaining strides (contiguous ones when omitted)."""
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    Lq = Lq if lq is None else lq
+    Lk = Lk if lk is None else lk
+    desc = ra_attn_desc()
+    desc.batch, desc.hq, desc.hkv, desc.lq, desc.lk, desc.d = B, Hq, Hkv, Lq, Lk, d
+    desc.in_dtype = _dtype_code(q)
+    if out is not None:
+        desc.out_dtype = _dtype_code(out)
+        desc.out = strides_of(out)
+    else:
+        desc.out_dtype = desc.in_dtype if out_dtype is None else out_dtype
+        desc.out = ra_strides(Hq * Lq * d, Lq * d, d)
+    desc.q, desc.k, desc.v = strides_of(q), strides_of(k), strides_of(v)
+    desc.ml = ra_strides(ml.stride(0), ml.stride(1), 1) if ml is not None else ra_strides(Hq * Lq, Lq, 1)
+    desc.o = strides_of(o) if o is not None else ra_strides(Hq * Lq * d, Lq * d, d)
+    desc.scale = scale
+    desc.reserved = 0
+    return desc
+
+
+def ring_desc(q, k, v, *, seq: int, n_chunks: int, layout, causal: bool, q_chunk_first: int = 0,
+              q_chunk_count: Optional[int] = None, out=None, lse=None, out_dtype=None,
+              scale: float = 0.0) -> ra_ring_desc:
+    """Descriptor for :func:`ra_ring_fwd`: q holds the query chunks back to back,
+    k and v all ``n_chunks`` chunks (chunk-major physical order)."""
+    L = seq // n_chunks
+    if q_chunk_count is None:
+        q_chunk_count = q.shape[2] // L
+    r = ra_ring_desc()
+    r.attn = attn_desc(q, k, v, out=out, ml=lse, out_dtype=out_dtype, scale=scale, lq=L, lk=L)
+    if lse is None:
+        Hq = q.shape[1]
+        r.attn.ml = ra_strides(Hq * q_chunk_count * L, q_chunk_count * L, 1)
+    r.seq = seq
+    r.n_chunks = n_chunks
+    r.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    r.causal = 1 if causal else 0
+    r.q_chunk_first = q_chunk_first
+    r.q_chunk_count = q_chunk_count
+    r.reserved = 0
+    return r
+
+
+# ---- entry points -----------------------------------------------------------
+
+def ra_abi_version() -> int:
+    return _lib.ra_abi_version()
+
+
+def ra_status_str(status: int) -> str:
+    return _lib.ra_status_str(status).decode()
+
+
+def ra_last_error() -> str:
+    return _lib.ra_last_error().decode()
+
+
+def ra_state_init(desc: ra_attn_desc, m, l, o, stream=None):
+    _check(_lib.ra_state_init(ctypes.byref(desc), _ptr(m), _ptr(l), _ptr(o), _stream(stream)), "ra_state_init")
+
+
+def ra_chunk_fwd(desc: ra_attn_desc, q, k, v, m, l, o, causal_delta: int = 0, causal: bool = False, stream=None):
+    _check(_lib.ra_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(l), _ptr(o),
+                             int(causal_delta), 1 if causal else 0, _stream(stream)), "ra_chunk_fwd")
+
+
+def ra_finalize(desc: ra_attn_desc, m, l, o, out, lse=None, stream=None):
+    _check(_lib.ra_finalize(ctypes.byref(desc), _ptr(m), _ptr(l), _ptr(o), _ptr(out), _ptr(lse),
+                            _stream(stream)), "ra_finalize")
+
+
+def ra_merge(desc: ra_attn_desc, lse_a, o_a, lse_b, o_b, lse_out, o_out, stream=None):
+    _check(_lib.ra_merge(ctypes.byref(desc), _ptr(lse_a), _ptr(o_a), _ptr(lse_b), _ptr(o_b), _ptr(lse_out),
+                         _ptr(o_out), _stream(stream)), "ra_merge")
+
+
+def ra_ring_workspace_bytes(desc: ra_ring_desc) -> int:
+    return int(_lib.ra_ring_workspace_bytes(ctypes.byref(desc)))
+
+
+def ra_ring_fwd(desc: ra_ring_desc, q, k, v, out, lse=None, workspace=None, workspace_bytes: int = 0,
+                stream=None):
+    _check(_lib.ra_ring_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+                            workspace_bytes, _stream(stream)), "ra_ring_fwd")
+
+
+def ra_layout_positions(layout, seq: int, n_chunks: int, chunk: int) -> np.ndarray:
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    L = seq // n_chunks if n_chunks > 0 else 0
+    pos = np.zeros(max(L, 1), dtype=np.int64)
+    _check(_lib.ra_layout_positions(lay, seq, n_chunks, chunk, pos.ctypes.data_as(_P(ctypes.c_int64))),
+           "ra_layout_positions")
+    return pos[:L]
+
+
+def ra_ring_schedule(desc: ra_ring_desc, q_chunk: int) -> list[dict]:
+    n = ctypes.c_int32(0)
+    st = _lib.ra_ring_schedule(ctypes.byref(desc), q_chunk, None, 0, ctypes.byref(n))
+    if n.value == 0:
+        _check(st, "ra_ring_schedule")
+    tasks = (ra_task * n.value)()
+    _check(_lib.ra_ring_schedule(ctypes.byref(desc), q_chunk, tasks, n.value, ctypes.byref(n)), "ra_ring_schedule")
+    return [dict(step=t.step, kv_chunk=t.kv_chunk, q_row0=t.q_row0, q_len=t.q_len, kv_row0=t.kv_row0,
+                 kv_len=t.kv_len, delta=t.delta, kind=t.kind) for t in tasks]
+
+
+def ra_permute(layout, to_chunked: bool, src, dst, n_chunks: int, stream=None):
+    """src, dst: contiguous [B, H, S, d] tensors of the same dtype."""
+    B, H, S, d = src.shape
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    _check(_lib.ra_permute(lay, 1 if to_chunked else 0, B, H, S, n_chunks, d, _dtype_code(src), _ptr(src),
+                           _ptr(dst), _stream(stream)), "ra_permute")
