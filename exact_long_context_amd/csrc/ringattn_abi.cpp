@@ -107,15 +107,16 @@ void fill_common(ra::FwdArgs& a, const ra_attn_desc* d, const void* q, const voi
   a.scale_log2 = log2_scale(d);
 }
 
-// Work decomposition.  bf16: 4 waves of 64 rows per workgroup; the waves are
+// Work decomposition.  bf16: 8 waves of 32 rows per workgroup; the waves are
 // query heads of one KV head when the group size allows (GQA shares every K/V
 // tile over the heads), else consecutive row blocks of one head.  fp32: one
 // wave of 64 rows.
 ra_status plan_launch(ra::FwdArgs& a, bool bf16, int64_t seg_len, int32_t nseg_q, int32_t q_count) {
   const int32_t G = a.hq / a.hkv;
   if (bf16) {
+    // 8 waves of 32 rows
     a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
-    a.rows_per_wg = 64 * 4 / a.heads_per_wg;
+    a.rows_per_wg = 32 * 8 / a.heads_per_wg;
   } else {
     a.heads_per_wg = 1;
     a.rows_per_wg = 64;
