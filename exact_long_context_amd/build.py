@@ -20,6 +20,9 @@ LIB = os.path.join(PKG, "libringattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["ringattn_abi.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "elementwise.hip"]
+# the bf16 kernel never produces NaN (masked scores are -inf, masked keys meet
+# zero V); without this flag every v_max_f32 gets a quieting max(x, x) first
+EXTRA_FLAGS = {"attn_fwd_bf16.hip": ["-fno-honor-nans"]}
 
 ARCH = "gfx950"
 # packed fp32 VALU forms are disabled for every HIP object (see the design notes)
@@ -38,7 +41,7 @@ def _hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [_hipcc(), *lang, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *lang, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

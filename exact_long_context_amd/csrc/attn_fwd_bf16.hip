@@ -38,9 +38,12 @@
 //     keys; the V^T operand is then one 16-byte LDS read.
 //   * V is transposed while it is staged (2 keys x 8 dv register transposes
 //     with v_perm_b32), so both MFMA operands come from ds_read_b128.
-//   * K is copied global -> LDS directly (global_load_lds_dwordx4) with a
-//     16-byte chunk swizzle chosen per lane.
+//   * K goes global -> registers -> LDS with a 16-byte chunk swizzle (a direct
+//     global -> LDS copy would make the compiler wait for it before every LDS
+//     read, which exposes the load latency).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "fwd_common.h"
 #include "kernels.h"
@@ -65,7 +68,7 @@ constexpr int KROWB = D * 2;       // bytes of one K row in LDS
 constexpr int VROWB = BN * 2;      // bytes of one V^T row (64 keys) in LDS
 constexpr int KTILE = BN * KROWB;  // 16 KiB
 constexpr int VTILE = D * VROWB;   // 16 KiB
-constexpr int NKBUF = 2, NVBUF = 3;
+constexpr int NKBUF = 2, NVBUF = 2;
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
@@ -76,9 +79,13 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 __device__ __forceinline__ int kswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int k_off(int row, int chunk) { return row * KROWB + ((chunk ^ kswz(row)) << 4); }
 // V^T tile: row dv holds 64 keys (8 chunks of 16 B); chunk c of row dv is
-// stored at c ^ ((dv >> 1) & 7).  A V operand read touches 16 consecutive dv
-// rows at one chunk: (dv parity, swizzled chunk) are then all distinct.
-__device__ __forceinline__ int v_off(int dv, int chunk) { return dv * VROWB + ((chunk ^ ((dv >> 1) & 7)) << 4); }
+// stored at c ^ vswz(dv).  A V operand read touches 16 consecutive dv rows
+// (aligned to 16) at one chunk, where vswz takes 8 distinct values on each
+// parity class; a staging write touches rows 8vc + j for 16 values of vc,
+// where (parity, vswz) is made distinct by the write order below.  Both are
+// then free of bank conflicts.
+__device__ __forceinline__ int vswz(int dv) { return ((dv >> 1) ^ (dv >> 4)) & 7; }
+__device__ __forceinline__ int v_off(int dv, int chunk) { return dv * VROWB + ((chunk ^ vswz(dv)) << 4); }
 // Row of the K tile that feeds MFMA row i of a 32-key block.
 __device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
@@ -163,48 +170,73 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const float c2 = a.scale_log2;
   const bool causal = a.causal != 0;
 
-  // ---- staging assignments
-  // K: instruction i of wave w fills LDS rows 4(8i + w) .. +3; lane -> (row, stored chunk)
-  const int k_row_in4 = lane >> 4;
-  const int k_cpos = lane & 15;
+  // ---- staging: buffer loads relative to the current KV segment; rows past
+  // the segment end are out of the buffer's range and read as zero (masked
+  // keys must meet finite V), so the loads need no bounds branches.
+  // K: thread -> 16-byte chunk kc of rows kr and kr + 32
+  const int kc = tid & 15;
+  const int kr = tid >> 4;
+  const uint32_t koff0 = (uint32_t)(kr * kss + kc * 16), koff1 = (uint32_t)((kr + 32) * kss + kc * 16);
   // V: thread -> dv chunk vc (dv 8vc .. 8vc+7) and key pair vk (keys 2vk, 2vk+1)
   const int vc = tid & 15;
   const int vk = tid >> 4;
-  u32x4 vst[2];
+  const uint32_t voff0 = (uint32_t)(2 * vk * vss + vc * 16), voff1 = (uint32_t)((2 * vk + 1) * vss + vc * 16);
+  u32x4 kst[2], vst[2];
 
-  auto k_issue = [&](const TileInfo& t, unsigned char* kb) {
-    const int last = t.kv_len - 1 - t.k0;  // last valid tile row
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int grp = 8 * i + wave;
-      const int row = 4 * grp + k_row_in4;
-      const int src_row = row < last ? row : last;  // rows past the segment end repeat a valid row
-      const int chunk = k_cpos ^ kswz(row);
-      const unsigned char* src = Kg + (t.kv_row + t.k0 + src_row) * kss + chunk * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(kb + grp * 1024), 16, 0, 0);
-    }
+  auto load_tile = [&](const TileInfo& t) {
+    // an exhausted cursor gets an empty buffer: its loads return zeros
+    const uint32_t kbytes = t.valid ? (uint32_t)((t.kv_len - 1) * kss + KROWB) : 0u;
+    const uint32_t vbytes = t.valid ? (uint32_t)((t.kv_len - 1) * vss + KROWB) : 0u;
+    const int64_t row = t.valid ? t.kv_row : 0;
+    const __amdgpu_buffer_rsrc_t kr_ =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + row * kss), (short)0, (int)kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr_ =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + row * vss), (short)0, (int)vbytes, 0x00020000);
+    const int ks0 = t.valid ? (int)(t.k0 * kss) : 0, vs0 = t.valid ? (int)(t.k0 * vss) : 0;
+    kst[0] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff0, ks0, 0);
+    kst[1] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff1, ks0, 0);
+    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff0, vs0, 0);
+    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff1, vs0, 0);
   };
-  auto v_load = [&](const TileInfo& t) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int r = 2 * vk + e;
-      if (t.k0 + r < t.kv_len) vst[e] = *(const u32x4*)(Vg + (t.kv_row + t.k0 + r) * vss + vc * 16);
-      else vst[e] = u32x4{0u, 0u, 0u, 0u};  // masked keys must meet finite V
-    }
+  auto k_store = [&](unsigned char* kb) {
+    *(u32x4*)(kb + k_off(kr, kc)) = kst[0];
+    *(u32x4*)(kb + k_off(kr + 32, kc)) = kst[1];
   };
   auto v_store = [&](unsigned char* vb) {
-    // 2 keys x 8 dv -> 8 dv rows x 2 keys (4 bytes each)
+    // 2 keys x 8 dv -> 8 dv rows x 2 keys (4 bytes each); lanes with odd vc
+    // write the odd row of each pair first, which spreads every write
+    // instruction over all banks
+    const bool odd = vc & 1;
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
       const unsigned ev = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], 0x05040100u);
       const unsigned od = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], 0x07060302u);
-      const int dv = 8 * vc + 2 * pr;
-      *(unsigned*)(vb + v_off(dv, vk >> 2) + 4 * (vk & 3)) = ev;
-      *(unsigned*)(vb + v_off(dv + 1, vk >> 2) + 4 * (vk & 3)) = od;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int par = b ^ (int)odd;
+        const int dv = 8 * vc + 2 * pr + par;
+        *(unsigned*)(vb + v_off(dv, vk >> 2) + 4 * (vk & 3)) = par ? od : ev;
+      }
     }
   };
 
-  // S^T of one tile for this wave: s[kb] covers keys kb*32 .. +31 (rows permuted by kperm)
+  // Per-lane LDS offsets of the MFMA operands inside one tile buffer.  The
+  // swizzle is an XOR with a per-lane value, so each distinct chunk gets its
+  // own precomputed offset; buffer and block offsets fold into immediates.
+  int k_lane[8];  // K operand, 16-key step ks: row kperm(l32), chunk 2ks + g
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_lane[ks] = k_off(kperm(l32), 2 * ks + g);
+  // V^T operand of (dvb, b2, mm): row dvb*32 + l32, chunk c = 4b2 + 2mm + g.
+  // vswz(dvb*32 + l32) = lsw ^ (2 dvb mod 8), so the stored chunk is
+  // (x + g) ^ lsw with the even compile-time x = (4b2 + 2mm) ^ (2 dvb mod 8).
+  int v_lane[4];
+  {
+    const int lsw = ((l32 >> 1) & 7) ^ (l32 >> 4);
+#pragma unroll
+    for (int xh = 0; xh < 4; ++xh) v_lane[xh] = l32 * VROWB + (((2 * xh + g) ^ lsw) << 4);
+  }
+
+  // S^T of one tile for this wave: s[b2] covers keys b2*32 .. +31 (rows permuted by kperm)
   auto qk = [&](const unsigned char* kb, f32x16 (&s)[2]) {
     s[0] = f32x16{};
     s[1] = f32x16{};
@@ -212,7 +244,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
-        const bf16x8 kf = *(const bf16x8*)(kb + k_off(b2 * 32 + kperm(l32), 2 * ks + g));
+        const bf16x8 kf = *(const bf16x8*)(kb + b2 * 32 * KROWB + k_lane[ks]);
         s[b2] = mfma(kf, qf[ks], s[b2]);
       }
   };
@@ -259,7 +291,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // P^T B operands from S^T: pf[b2][mm] holds tile keys b2*32 + 16mm + 8g + 0..7
   auto softmax_p = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2]) {
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float rs = 0.f;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
@@ -271,9 +303,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
           pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[b2][mm * 8 + e + 1], c2, -m_use));
           pf[b2][mm][e] = pr[0];
           pf[b2][mm][e + 1] = pr[1];
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, rs, false);
+          float& r = rs[2 * b2 + mm];
+          r = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, r, false);
         }
-    l_run += rs;
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
   auto pv = [&](const unsigned char* vb, const bf16x8 (&pf)[2][2]) {
 #pragma unroll
@@ -282,7 +315,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int dvb = 0; dvb < 4; ++dvb) {
-          const bf16x8 vf = *(const bf16x8*)(vb + v_off(dvb * 32 + l32, 4 * b2 + 2 * mm + g));
+          const int x = (4 * b2 + 2 * mm) ^ ((2 * dvb) & 7);
+          const bf16x8 vf = *(const bf16x8*)(vb + dvb * 32 * VROWB + v_lane[x >> 1]);
           acc[dvb] = mfma(vf, pf[b2][mm], acc[dvb]);
         }
   };
@@ -295,16 +329,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   TileInfo t_nx1 = tile_info(nx2);
   if (!nx2.done) nx2.advance();
 
-  if (t_cur.valid) {
-    k_issue(t_cur, kbase);
-    v_load(t_cur);
-    v_store(vbase);
-  }
-  if (t_nx1.valid) {
-    k_issue(t_nx1, kbase + KTILE);
-    v_load(t_nx1);
-    v_store(vbase + VTILE);
-  }
+  // tile 0 -> buffers 0, tile 1 -> buffers 1
+  load_tile(t_cur);
+  k_store(kbase);
+  v_store(vbase);
+  load_tile(t_nx1);
+  k_store(kbase + KTILE);
+  v_store(vbase + VTILE);
+  // retire every prologue load (Q, state) here so that the loop's first LDS
+  // read does not wait on the loads the loop itself issues
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt untouched
   __syncthreads();
 
   f32x16 s_a[2], s_b[2];
@@ -313,37 +347,54 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     if (tile_needs_mask(t_cur)) apply_mask(s_a, t_cur);
     update_ref(row_max(s_a));
   }
+  __syncthreads();  // every wave is done with K buffer 0 before tile 2 lands there
 
-  int kb_j = 0;  // K buffer of tile j (tile j+1 is in kb_j ^ 1)
-  int vb_j = 0;  // V buffer of tile j (j+1 in (vb_j+1)%3, j+2 in (vb_j+2)%3)
-  // one ring iteration; s_cur holds S^T of tile j (masked, reference updated)
-  auto iteration = [&](f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+  // One ring iteration.  Tile j sits in K / V buffers P, tile j+1 in buffers
+  // P ^ 1; s_cur holds S^T of tile j (masked, reference already updated).
+  auto iteration = [&](auto pc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    constexpr int P = decltype(pc)::value;
     const TileInfo t_nx2 = tile_info(nx2);
-    if (t_nx2.valid) {
-      k_issue(t_nx2, kbase + kb_j * KTILE);  // K_j's buffer is free: QK(j) ran last iteration
-      v_load(t_nx2);
-    }
+    load_tile(t_nx2);
     // phase A: QK(j+1) || exponentials of tile j
     bf16x8 pf[2][2];
-    qk(kbase + (kb_j ^ 1) * KTILE, s_nxt);
+    qk(kbase + (P ^ 1) * KTILE, s_nxt);
     softmax_p(s_cur, pf);
-    if (t_nx1.valid && tile_needs_mask(t_nx1)) apply_mask(s_nxt, t_nx1);
-    // phase B: PV(j) || max of tile j+1, V(j+2) transpose into LDS
-    pv(vbase + vb_j * VTILE, pf);
-    const float mx_next = row_max(s_nxt);
-    v_store(vbase + (vb_j >= 1 ? vb_j - 1 : 2) * VTILE);  // (vb_j + 2) % 3; stale data if no tile j+2
+    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // the four global loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // first K operand reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K operand read
+    }
+    // phase B: PV(j) || max of tile j+1; K of tile j+2 into K buffer P
+    pv(vbase + P * VTILE, pf);
+    float mx_next = row_max(s_nxt);
+    k_store(kbase + P * KTILE);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // first V operand reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // K stores
+    // tiles that cross the diagonal or the segment end: mask, then redo the max
+    if (t_nx1.valid && tile_needs_mask(t_nx1)) {
+      apply_mask(s_nxt, t_nx1);
+      mx_next = row_max(s_nxt);
+    }
     if (t_nx1.valid) update_ref(mx_next);
-    __syncthreads();  // also waits for the direct-to-LDS K copies
+    __syncthreads();
+    v_store(vbase + P * VTILE);  // V of tile j+2: every wave has finished PV(j)
     t_cur = t_nx1;
     t_nx1 = t_nx2;
     if (!nx2.done) nx2.advance();
-    kb_j ^= 1;
-    vb_j = vb_j == 2 ? 0 : vb_j + 1;
   };
   while (t_cur.valid) {
-    iteration(s_a, s_b);
+    iteration(std::integral_constant<int, 0>{}, s_a, s_b);
     if (!t_cur.valid) break;
-    iteration(s_b, s_a);
+    iteration(std::integral_constant<int, 1>{}, s_b, s_a);
   }
 
   // ---- epilogue
