@@ -5,9 +5,9 @@
 //   * its Q tile as MFMA B operands (32 rows x 128 bf16 = 32 VGPRs),
 //   * the transposed output accumulator O^T (128 x 32 fp32 = 64 registers),
 //   * the reference max m, the exact running max and a per-lane partial l.
-// K and V tiles of 64 keys are staged once per workgroup through LDS and read
-// by all 8 waves; with grouped-query attention the waves are the query heads
-// of one KV head (4 heads x 64 rows), so each K/V byte fetched serves 4 heads.
+// K and V tiles of 64 keys are staged through LDS and read by all 8 waves;
+// with grouped-query attention the waves are the query heads of one KV head
+// (4 heads x 64 rows), so each K/V byte fetched serves 4 heads.
 //
 // Per tile (the online-softmax update of blockwise_attention /
 // ring_attention_forward on the youngju.dev page, and the m / l / o
@@ -22,12 +22,18 @@
 // on few tiles.  The exact running maximum is tracked beside it for the state
 // handed back by the chunk entry point.
 //
-// Software pipeline inside each wave, iteration j:
-//   phase A: MFMA  S_{j+1} = K_{j+1} Q^T   ||  VALU  P_j = 2^(c S_j - m), rowsum
-//   phase B: MFMA  O^T += V_j^T P_j^T      ||  VALU  mask / max of S_{j+1},
-//                                                    V_{j+2} transpose into LDS
-// so the exponentials of one tile hide under the matrix work of the next.
-// LDS holds K for tiles j+1, j+2 and V^T for tiles j, j+1, j+2 (80 KiB).
+// Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the SIMDs
+// pairwise.  Each wave alternates two kinds of slot, separated by workgroup
+// barriers, with group B one slot behind group A:
+//   matrix slot : S^T of tile n and O^T += V^T P^T of tile n-1 (32 MFMA,
+//                 operand reads issued ahead of use)
+//   vector slot : mask / max / exponentials of the tile whose S^T it holds,
+//                 plus the group's half of the K / V staging (LDS writes,
+//                 global loads one iteration ahead)
+// so while one wave of a SIMD runs its matrix slot the other runs its vector
+// slot, and the matrix core and the vector ALU work at the same time.
+// Iteration n stages K(n+1) into K buffer (n+1) % 2 and V(n) into V buffer
+// n % 2 (64 KiB of LDS in all).
 //
 // Layout tricks:
 //   * S is computed transposed (keys x queries): one query per lane, 32 keys
@@ -38,9 +44,8 @@
 //     keys; the V^T operand is then one 16-byte LDS read.
 //   * V is transposed while it is staged (2 keys x 8 dv register transposes
 //     with v_perm_b32), so both MFMA operands come from ds_read_b128.
-//   * K goes global -> registers -> LDS with a 16-byte chunk swizzle (a direct
-//     global -> LDS copy would make the compiler wait for it before every LDS
-//     read, which exposes the load latency).
+//   * K and V load through buffer resources bounded by the KV segment: rows
+//     past the segment end read as zero, with no per-row branches.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -68,7 +73,6 @@ constexpr int KROWB = D * 2;       // bytes of one K row in LDS
 constexpr int VROWB = BN * 2;      // bytes of one V^T row (64 keys) in LDS
 constexpr int KTILE = BN * KROWB;  // 16 KiB
 constexpr int VTILE = D * VROWB;   // 16 KiB
-constexpr int NKBUF = 2, NVBUF = 2;
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
@@ -112,15 +116,17 @@ __device__ __forceinline__ TileInfo tile_info(const TileCursor<BN>& c) {
 }
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NKBUF * KTILE + NVBUF * VTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * KTILE + 2 * VTILE];
   unsigned char* const kbase = smem;
-  unsigned char* const vbase = smem + NKBUF * KTILE;
+  unsigned char* const vbase = smem + 2 * KTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int grp = wave >> 2;       // 0: group A, 1: group B
+  const int gtid = tid & 255;      // thread index inside the group
   const int l32 = lane & 31;
-  const int g = lane >> 5;  // half-wave
+  const int g = lane >> 5;         // half-wave
 
   const WorkItem it = decode_work(a, blockIdx.x);
   const QGeom qg = query_geom(a, it);
@@ -170,39 +176,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const float c2 = a.scale_log2;
   const bool causal = a.causal != 0;
 
-  // ---- staging: buffer loads relative to the current KV segment; rows past
-  // the segment end are out of the buffer's range and read as zero (masked
-  // keys must meet finite V), so the loads need no bounds branches.
-  // K: thread -> 16-byte chunk kc of rows kr and kr + 32
-  const int kc = tid & 15;
-  const int kr = tid >> 4;
-  const uint32_t koff0 = (uint32_t)(kr * kss + kc * 16), koff1 = (uint32_t)((kr + 32) * kss + kc * 16);
+  // ---- staging: each group moves its half of every tile (keys 32 grp ..
+  // 32 grp + 31).  Buffer loads relative to the tile's KV segment; rows past
+  // the segment end are out of range and read as zero (masked keys must meet
+  // finite V), so no bounds branches are needed.
+  // K: thread -> 16-byte chunk kc of rows kr and kr + 16
+  const int kc = gtid & 15;
+  const int kr = 32 * grp + (gtid >> 4);
+  const uint32_t koff0 = (uint32_t)(kr * kss + kc * 16), koff1 = (uint32_t)((kr + 16) * kss + kc * 16);
   // V: thread -> dv chunk vc (dv 8vc .. 8vc+7) and key pair vk (keys 2vk, 2vk+1)
-  const int vc = tid & 15;
-  const int vk = tid >> 4;
+  const int vc = gtid & 15;
+  const int vk = 16 * grp + (gtid >> 4);
   const uint32_t voff0 = (uint32_t)(2 * vk * vss + vc * 16), voff1 = (uint32_t)((2 * vk + 1) * vss + vc * 16);
   u32x4 kst[2], vst[2];
 
-  auto load_tile = [&](const TileInfo& t) {
-    // an exhausted cursor gets an empty buffer: its loads return zeros
-    const uint32_t kbytes = t.valid ? (uint32_t)((t.kv_len - 1) * kss + KROWB) : 0u;
-    const uint32_t vbytes = t.valid ? (uint32_t)((t.kv_len - 1) * vss + KROWB) : 0u;
-    const int64_t row = t.valid ? t.kv_row : 0;
-    const __amdgpu_buffer_rsrc_t kr_ =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + row * kss), (short)0, (int)kbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr_ =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + row * vss), (short)0, (int)vbytes, 0x00020000);
-    const int ks0 = t.valid ? (int)(t.k0 * kss) : 0, vs0 = t.valid ? (int)(t.k0 * vss) : 0;
-    kst[0] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff0, ks0, 0);
-    kst[1] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff1, ks0, 0);
-    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff0, vs0, 0);
-    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff1, vs0, 0);
+  // an exhausted cursor gets an empty buffer: its loads return zeros
+  auto load_k = [&](const TileInfo& t) __attribute__((always_inline)) {
+    const uint32_t bytes = t.valid ? (uint32_t)((t.kv_len - 1) * kss + KROWB) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (t.valid ? t.kv_row : 0) * kss), (short)0, (int)bytes,
+                                          0x00020000);
+    const int so = t.valid ? (int)(t.k0 * kss) : 0;
+    kst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff0, so, 0);
+    kst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff1, so, 0);
   };
-  auto k_store = [&](unsigned char* kb) {
+  auto load_v = [&](const TileInfo& t) __attribute__((always_inline)) {
+    const uint32_t bytes = t.valid ? (uint32_t)((t.kv_len - 1) * vss + KROWB) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (t.valid ? t.kv_row : 0) * vss), (short)0, (int)bytes,
+                                          0x00020000);
+    const int so = t.valid ? (int)(t.k0 * vss) : 0;
+    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff0, so, 0);
+    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff1, so, 0);
+  };
+  auto store_k = [&](unsigned char* kb) __attribute__((always_inline)) {
     *(u32x4*)(kb + k_off(kr, kc)) = kst[0];
-    *(u32x4*)(kb + k_off(kr + 32, kc)) = kst[1];
+    *(u32x4*)(kb + k_off(kr + 16, kc)) = kst[1];
   };
-  auto v_store = [&](unsigned char* vb) {
+  auto store_v = [&](unsigned char* vb) __attribute__((always_inline)) {
     // 2 keys x 8 dv -> 8 dv rows x 2 keys (4 bytes each); lanes with odd vc
     // write the odd row of each pair first, which spreads every write
     // instruction over all banks
@@ -236,21 +247,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int xh = 0; xh < 4; ++xh) v_lane[xh] = l32 * VROWB + (((2 * xh + g) ^ lsw) << 4);
   }
 
-  // S^T of one tile for this wave: s[b2] covers keys b2*32 .. +31 (rows permuted by kperm)
-  auto qk = [&](const unsigned char* kb, f32x16 (&s)[2]) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        const bf16x8 kf = *(const bf16x8*)(kb + b2 * 32 * KROWB + k_lane[ks]);
-        s[b2] = mfma(kf, qf[ks], s[b2]);
-      }
-  };
   // Mask a tile: register r of block b2 in half-wave g is tile key
   // b2*32 + 16*(r/8) + 8g + r%8; it is hidden from this lane's row when key > lim.
-  auto apply_mask = [&](f32x16 (&s)[2], const TileInfo& t) {
+  f32x16 s[2];       // S^T of a tile, between its matrix slot and its vector slot
+  bf16x8 pf[2][2];   // P^T of a tile, between its vector slot and its PV MFMAs:
+                     // pf[b2][mm] holds tile keys b2*32 + 16mm + 8g + 0..7
+  auto apply_mask = [&](const TileInfo& t) __attribute__((always_inline)) {
     int64_t lim = (int64_t)t.kv_len - 1 - t.k0;
     if (causal) {
       const int64_t lc = (int64_t)my_p + t.delta - t.k0;
@@ -265,31 +267,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         s[b2][r] = kk > lim32 ? -INFINITY : s[b2][r];
       }
   };
-  auto row_max = [&](const f32x16 (&s)[2]) -> float {
+  auto tile_needs_mask = [&](const TileInfo& t) __attribute__((always_inline)) -> bool {
+    return (t.k0 + BN > t.kv_len) || (causal && (int64_t)(t.k0 + BN - 1) - p0 > t.delta);
+  };
+
+  // Vector work on a computed S^T: mask, maximum, reference update (rare O^T
+  // rescale), exponentials into P^T and the row sum.
+  auto softmax_tile = [&](const TileInfo& t) __attribute__((always_inline)) {
+    if (tile_needs_mask(t)) apply_mask(t);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    mx = fmaxf(mx, xor32(mx));
-    return mx * c2;
-  };
-  auto tile_needs_mask = [&](const TileInfo& t) -> bool {
-    return (t.k0 + BN > t.kv_len) || (causal && (int64_t)(t.k0 + BN - 1) - p0 > t.delta);
-  };
-  // Move the reference maximum if the tile maximum mx2 outgrew it; rescales O^T and l.
-  auto update_ref = [&](float mx2) {
-    m_max = fmaxf(m_max, mx2);
-    const bool grow = mx2 > m_ref + RESCALE_SLACK;  // also true when m_ref is -inf
+    mx = fmaxf(mx, xor32(mx)) * c2;
+    m_max = fmaxf(m_max, mx);
+    const bool grow = mx > m_ref + RESCALE_SLACK;  // also true when m_ref is -inf
     if (__any(grow)) {
-      const float m_new = grow ? mx2 : m_ref;
+      const float m_new = grow ? mx : m_ref;
       const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] *= alpha;
     }
-  };
-  // P^T B operands from S^T: pf[b2][mm] holds tile keys b2*32 + 16mm + 8g + 0..7
-  auto softmax_p = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2]) {
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -308,93 +307,121 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         }
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
-  auto pv = [&](const unsigned char* vb, const bf16x8 (&pf)[2][2]) {
+
+  // Matrix slot: S^T of the tile in K buffer KB and O^T += V^T P^T with the
+  // tile in V buffer VB; the two MFMA chains alternate so that each operand
+  // read has time to land.  At the ends of the stream one half works on stale
+  // or zero data: a QK with no tile behind it is never used, and the first PV
+  // multiplies P^T = 0 with a zeroed V buffer.
+  auto matrix_slot = [&](auto kbc, auto vbc) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
+    const unsigned char* kb = kbase + KB * KTILE;
+    const unsigned char* vb = vbase + VB * VTILE;
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      return *(const bf16x8*)(kb + (i & 1) * 32 * KROWB + k_lane[i >> 1]);
+    };
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
+      const int x = (4 * pb2 + 2 * pmm) ^ ((2 * dvb) & 7);
+      return *(const bf16x8*)(vb + dvb * 32 * VROWB + v_lane[x >> 1]);
+    };
+    constexpr int AHEAD = 2;  // operand reads in flight per chain
+    bf16x8 kq[AHEAD], vq[AHEAD];
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int i = 0; i < AHEAD; ++i) {
+      kq[i] = kread(i);
+      vq[i] = vread(i);
+    }
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int dvb = 0; dvb < 4; ++dvb) {
-          const int x = (4 * b2 + 2 * mm) ^ ((2 * dvb) & 7);
-          const bf16x8 vf = *(const bf16x8*)(vb + dvb * 32 * VROWB + v_lane[x >> 1]);
-          acc[dvb] = mfma(vf, pf[b2][mm], acc[dvb]);
-        }
+    for (int i = 0; i < 16; ++i) {
+      const bf16x8 kf = kq[i % AHEAD], vf = vq[i % AHEAD];
+      if (i + AHEAD < 16) {
+        kq[i % AHEAD] = kread(i + AHEAD);
+        vq[i % AHEAD] = vread(i + AHEAD);
+      }
+      // keep the reads issued ahead of the two MFMAs that follow
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = i >> 1, b2 = i & 1;
+      s[b2] = mfma(kf, qf[ks], s[b2]);
+      const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
+      acc[dvb] = mfma(vf, pf[pb2][pmm], acc[dvb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // ---- tile stream: cur = j (softmax / PV), nx1 = j+1 (QK), nx2 = j+2 (loads)
-  TileCursor<BN> nx2 = make_cursor<BN>(a, qg, wg_p_hi);
-  if (wg_p_hi < wg_p0) nx2.done = true;
-  TileInfo t_cur = tile_info(nx2);
-  if (!nx2.done) nx2.advance();
-  TileInfo t_nx1 = tile_info(nx2);
-  if (!nx2.done) nx2.advance();
+  // ---- tile stream: infos of tiles n-1 .. n+2 around loop iteration n
+  TileCursor<BN> cur = make_cursor<BN>(a, qg, wg_p_hi);
+  if (wg_p_hi < wg_p0) cur.done = true;
+  auto next_info = [&]() __attribute__((always_inline)) -> TileInfo {
+    const TileInfo t = tile_info(cur);
+    if (!cur.done) cur.advance();
+    return t;
+  };
+  TileInfo tm1;  // tile n-1
+  tm1.valid = false;
+  tm1.k0 = tm1.kv_len = tm1.delta = 0;
+  tm1.kv_row = 0;
+  TileInfo t0 = next_info();  // tile n
+  TileInfo t1 = next_info();  // tile n+1
+  TileInfo t2 = next_info();  // tile n+2
 
-  // tile 0 -> buffers 0, tile 1 -> buffers 1
-  load_tile(t_cur);
-  k_store(kbase);
-  v_store(vbase);
-  load_tile(t_nx1);
-  k_store(kbase + KTILE);
-  v_store(vbase + VTILE);
-  // retire every prologue load (Q, state) here so that the loop's first LDS
-  // read does not wait on the loads the loop itself issues
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt untouched
+  // prologue: K(0) into K buffer 0 (both groups, one half each), V buffer 1
+  // zeroed for the first PV, P^T zeroed; then the registers for the first
+  // staging: K(1) and V(0)
+  load_k(t0);
+  store_k(kbase);
+  *(u32x4*)(vbase + VTILE + tid * 32) = u32x4{0u, 0u, 0u, 0u};
+  *(u32x4*)(vbase + VTILE + tid * 32 + 16) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) pf[b2][mm] = bf16x8{};
+  load_k(t1);
+  load_v(t0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): retire every prologue load here
   __syncthreads();
 
-  f32x16 s_a[2], s_b[2];
-  if (t_cur.valid) {
-    qk(kbase, s_a);
-    if (tile_needs_mask(t_cur)) apply_mask(s_a, t_cur);
-    update_ref(row_max(s_a));
-  }
-  __syncthreads();  // every wave is done with K buffer 0 before tile 2 lands there
-
-  // One ring iteration.  Tile j sits in K / V buffers P, tile j+1 in buffers
-  // P ^ 1; s_cur holds S^T of tile j (masked, reference already updated).
-  auto iteration = [&](auto pc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+  // Loop iteration n (two slots, a barrier after each):
+  //   slot 1: A matrix (QK(n), PV(n-1))  |  B vector (softmax(n-1)), staging
+  //   slot 2: A vector (softmax(n)), staging  |  B matrix (QK(n), PV(n-1))
+  // Staging writes the group's halves of K(n+1) -> K buffer (n+1) % 2 and of
+  // V(n) -> V buffer n % 2, then loads K(n+2) and V(n+1).
+  auto staging = [&](auto pc) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    const TileInfo t_nx2 = tile_info(nx2);
-    load_tile(t_nx2);
-    // phase A: QK(j+1) || exponentials of tile j
-    bf16x8 pf[2][2];
-    qk(kbase + (P ^ 1) * KTILE, s_nxt);
-    softmax_p(s_cur, pf);
-    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // the four global loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // first K operand reads
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K operand read
-    }
-    // phase B: PV(j) || max of tile j+1; K of tile j+2 into K buffer P
-    pv(vbase + P * VTILE, pf);
-    float mx_next = row_max(s_nxt);
-    k_store(kbase + P * KTILE);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // first V operand reads
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // K stores
-    // tiles that cross the diagonal or the segment end: mask, then redo the max
-    if (t_nx1.valid && tile_needs_mask(t_nx1)) {
-      apply_mask(s_nxt, t_nx1);
-      mx_next = row_max(s_nxt);
-    }
-    if (t_nx1.valid) update_ref(mx_next);
-    __syncthreads();
-    v_store(vbase + P * VTILE);  // V of tile j+2: every wave has finished PV(j)
-    t_cur = t_nx1;
-    t_nx1 = t_nx2;
-    if (!nx2.done) nx2.advance();
+    store_k(kbase + (P ^ 1) * KTILE);
+    store_v(vbase + P * VTILE);
+    load_k(t2);
+    load_v(t1);
   };
-  while (t_cur.valid) {
-    iteration(std::integral_constant<int, 0>{}, s_a, s_b);
-    if (!t_cur.valid) break;
-    iteration(std::integral_constant<int, 1>{}, s_b, s_a);
+  auto iteration = [&](auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;   // n % 2
+    const std::integral_constant<int, P> kbc{};
+    const std::integral_constant<int, P ^ 1> vbc{};
+    if (grp == 0) {
+      matrix_slot(kbc, vbc);
+    } else {
+      if (tm1.valid) softmax_tile(tm1);
+      staging(pc);
+    }
+    __syncthreads();
+    if (grp == 0) {
+      if (t0.valid) softmax_tile(t0);
+      staging(pc);
+    } else {
+      matrix_slot(kbc, vbc);
+    }
+    __syncthreads();
+    tm1 = t0;
+    t0 = t1;
+    t1 = t2;
+    t2 = next_info();
+  };
+  while (t0.valid || tm1.valid) {
+    iteration(std::integral_constant<int, 0>{});
+    if (!(t0.valid || tm1.valid)) break;
+    iteration(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue
