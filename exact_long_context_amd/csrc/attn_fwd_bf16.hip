@@ -58,7 +58,6 @@ namespace ra {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -97,7 +96,18 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by lane l ^ 32.  v_permlane32_swap
+// exchanges the upper half of one operand with the lower half of the other,
+// so for every lane its two results are x[l] and x[l ^ 32] (in an order that
+// depends on the half); max and sum are symmetric in them.
+__device__ __forceinline__ float max_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct TileInfo {
   bool valid;
@@ -275,10 +285,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // rescale), exponentials into P^T and the row sum.
   auto softmax_tile = [&](const TileInfo& t) __attribute__((always_inline)) {
     if (tile_needs_mask(t)) apply_mask(t);
-    float mx = -INFINITY;
+    // two chains of three-input maxima over the lane's 32 scores
+    float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    mx = fmaxf(mx, xor32(mx)) * c2;
+    for (int r = 2; r < 16; r += 2) {
+      mx0 = fmaxf(fmaxf(mx0, s[0][r]), s[0][r + 1]);
+      mx1 = fmaxf(fmaxf(mx1, s[1][r]), s[1][r + 1]);
+    }
+    const float mx = max_pair32(fmaxf(mx0, mx1)) * c2;
     m_max = fmaxf(m_max, mx);
     const bool grow = mx > m_ref + RESCALE_SLACK;  // also true when m_ref is -inf
     if (__any(grow)) {
@@ -290,20 +304,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] *= alpha;
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    // The row sum adds the fp32 exponentials (four chains).  It is not taken
+    // with v_dot2 over the bf16 pairs: dot instructions wait for the matrix
+    // core, which the other wave of the SIMD keeps busy during this slot.
+    float rs[4];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          bf16x2 pr;
-          pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[b2][mm * 8 + e], c2, -m_use));
-          pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[b2][mm * 8 + e + 1], c2, -m_use));
-          pf[b2][mm][e] = pr[0];
-          pf[b2][mm][e + 1] = pr[1];
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b2][mm * 8 + e], c2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b2][mm * 8 + e + 1], c2, -m_use));
+          pf[b2][mm][e] = (__bf16)p0;
+          pf[b2][mm][e + 1] = (__bf16)p1;
           float& r = rs[2 * b2 + mm];
-          r = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, r, false);
+          r = e == 0 ? p0 + p1 : (r + p0) + p1;
         }
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
@@ -425,7 +441,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- epilogue
-  float lt = l_run + xor32(l_run);
+  float lt = sum_pair32(l_run);
   if (my_p >= qg.len) return;
   if (a.mode == MODE_RING) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
