@@ -68,19 +68,20 @@ constexpr int BN = 64;           // keys per tile
 constexpr int WAVE_ROWS = 32;    // query rows per wave
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int KROWB = D * 2;       // bytes of one K row in LDS
+constexpr int ROWB = D * 2;        // bytes of one K or V row in global memory
+constexpr int KROWB = ROWB + 16;   // LDS pitch of one K row (16 bytes of padding)
 constexpr int VROWB = BN * 2;      // bytes of one V^T row (64 keys) in LDS
-constexpr int KTILE = BN * KROWB;  // 16 KiB
+constexpr int KTILE = BN * KROWB;  // 17 KiB
 constexpr int VTILE = D * VROWB;   // 16 KiB
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
-// K tile: row-major, 16 chunks of 16 B per row; chunk c of row r is stored at
-// c ^ kswz(r).  A K operand read touches 16 rows (all distinct mod 16) at one
-// chunk, so the swizzle spreads it over every bank.
-__device__ __forceinline__ int kswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int k_off(int row, int chunk) { return row * KROWB + ((chunk ^ kswz(row)) << 4); }
+// K tile: row-major with a padded pitch of 272 bytes.  A K operand read
+// touches 16 distinct rows at one 16-byte chunk; the pitch moves each row by
+// four banks, so the read covers every bank once, and the addresses of the
+// eight 16-key steps differ by constants (one base register per lane).
+__device__ __forceinline__ int k_off(int row, int chunk) { return row * KROWB + (chunk << 4); }
 // V^T tile: row dv holds 64 keys (8 chunks of 16 B); chunk c of row dv is
 // stored at c ^ vswz(dv).  A V operand read touches 16 consecutive dv rows
 // (aligned to 16) at one chunk, where vswz takes 8 distinct values on each
@@ -109,24 +110,83 @@ __device__ __forceinline__ float sum_pair32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-struct TileInfo {
-  bool valid;
-  int32_t k0, kv_len, delta;
-  int64_t kv_row;
+// One run = the key rows of one KV segment that a workgroup visits: ring step
+// t, KV segment sb.  The table of all runs is built once per workgroup in LDS
+// (rows of the KV buffer, segment length, causal offset, keys to visit) so
+// that the per-tile bookkeeping is a few scalar adds.
+constexpr int MAX_RUNS = BF16_MAX_RUNS;
+struct Run {
+  int32_t kv_row;  // buffer row of the segment's row 0
+  int32_t kv_len;  // rows in the segment
+  int32_t delta;   // causal offset, clamped to [-(2^30), 2^30]
+  int32_t k_end;   // keys to visit (0: nothing in this run)
 };
 
-__device__ __forceinline__ TileInfo tile_info(const TileCursor<BN>& c) {
-  TileInfo t;
-  t.valid = !c.done;
-  t.k0 = c.k0;
-  t.kv_len = c.kv_len;
-  t.delta = c.delta;
-  t.kv_row = c.kv_row;
-  return t;
+__device__ __forceinline__ Run make_run(const FwdArgs& a, const QGeom& qg, int32_t p_hi, int32_t r) {
+  Run e;
+  int64_t dl = 0;
+  if (a.mode == MODE_CHUNK) {
+    e.kv_row = 0;
+    e.kv_len = a.lk;
+    dl = a.delta;
+  } else {
+    const int32_t nseg = num_segments(a.layout);
+    const int32_t t = nseg == 2 ? (r >> 1) : r;
+    const int32_t sb = nseg == 2 ? (r & 1) : 0;
+    const int32_t j = ring_kv_chunk(qg.qchunk, t, a.n_chunks);
+    const Segment ks = segment_l(a.layout, a.lq, a.n_chunks, j, sb);
+    e.kv_row = j * a.lq + ks.row0;
+    e.kv_len = ks.len;
+    dl = a.causal ? pair_delta(qg.seg, ks) : 0;
+  }
+  int64_t end = e.kv_len;
+  if (a.causal) {
+    const int64_t x = (int64_t)p_hi + dl + 1;
+    end = x < 0 ? 0 : (x < end ? x : end);
+  }
+  e.k_end = (int32_t)end;
+  const int64_t lim = (int64_t)1 << 30;
+  e.delta = (int32_t)(dl > lim ? lim : (dl < -lim ? -lim : dl));
+  return e;
 }
+
+// Wave-uniform walk over the run table: tiles of BN keys in ring order.
+struct RunCursor {
+  int32_t ri, nruns, k0, kv_row, kv_len, delta, k_end;
+  bool done;
+  __device__ __forceinline__ void load(const Run* runs) {
+    const Run e = runs[ri];
+    kv_row = __builtin_amdgcn_readfirstlane(e.kv_row);
+    kv_len = __builtin_amdgcn_readfirstlane(e.kv_len);
+    delta = __builtin_amdgcn_readfirstlane(e.delta);
+    k_end = __builtin_amdgcn_readfirstlane(e.k_end);
+  }
+  __device__ __forceinline__ void skip_empty(const Run* runs) {
+    while (!done && k0 >= k_end) {
+      if (++ri >= nruns) { done = true; break; }
+      k0 = 0;
+      load(runs);
+    }
+  }
+  __device__ __forceinline__ void start(const Run* runs, int32_t n) {
+    nruns = n; ri = 0; k0 = 0; done = n <= 0;
+    kv_row = kv_len = delta = k_end = 0;
+    if (!done) { load(runs); skip_empty(runs); }
+  }
+  __device__ __forceinline__ void advance(const Run* runs) {
+    k0 += BN;
+    skip_empty(runs);
+  }
+};
+
+struct TileInfo {
+  bool valid;
+  int32_t k0, kv_len, delta, kv_row;
+};
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * KTILE + 2 * VTILE];
+  __shared__ Run runs[MAX_RUNS];
   unsigned char* const kbase = smem;
   unsigned char* const vbase = smem + 2 * KTILE;
 
@@ -146,12 +206,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int wg_p0 = it.tile * a.rows_per_wg;
   const int p0 = wg_p0 + (wave / HP) * WAVE_ROWS;  // first row of this wave in the segment
   const int wg_p_hi = min(wg_p0 + a.rows_per_wg, qg.len) - 1;
+  const int nruns = a.mode == MODE_CHUNK ? 1 : a.n_chunks * num_segments(a.layout);
+  for (int r = tid; r < nruns; r += NTHREADS) runs[r] = make_run(a, qg, wg_p_hi, r);
   const int my_p = p0 + l32;                        // this lane's query row
 
   const __bf16* Qg = (const __bf16*)a.q + (int64_t)it.b * a.q_sb + (int64_t)h * a.q_sh;
   const unsigned char* Kg = (const unsigned char*)a.k + ((int64_t)it.b * a.k_sb + (int64_t)it.kvh * a.k_sh) * 2;
   const unsigned char* Vg = (const unsigned char*)a.v + ((int64_t)it.b * a.v_sb + (int64_t)it.kvh * a.v_sh) * 2;
-  const int64_t kss = a.k_ss * 2, vss = a.v_ss * 2;  // row strides in bytes
+  // row strides in bytes; every byte offset inside one head's K or V fits in
+  // 31 bits (checked on the host)
+  const uint32_t kss = (uint32_t)(a.k_ss * 2), vss = (uint32_t)(a.v_ss * 2);
 
   // ---- Q as B operands: qf[ks] = Q[row my_p][ks*16 + 8g .. +8]
   bf16x8 qf[8];
@@ -193,29 +257,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // K: thread -> 16-byte chunk kc of rows kr and kr + 16
   const int kc = gtid & 15;
   const int kr = 32 * grp + (gtid >> 4);
-  const uint32_t koff0 = (uint32_t)(kr * kss + kc * 16), koff1 = (uint32_t)((kr + 16) * kss + kc * 16);
+  const uint32_t koff0 = kr * kss + kc * 16, koff1 = (kr + 16) * kss + kc * 16;
   // V: thread -> dv chunk vc (dv 8vc .. 8vc+7) and key pair vk (keys 2vk, 2vk+1)
   const int vc = gtid & 15;
   const int vk = 16 * grp + (gtid >> 4);
-  const uint32_t voff0 = (uint32_t)(2 * vk * vss + vc * 16), voff1 = (uint32_t)((2 * vk + 1) * vss + vc * 16);
+  const uint32_t voff0 = 2 * vk * vss + vc * 16, voff1 = (2 * vk + 1) * vss + vc * 16;
   u32x4 kst[2], vst[2];
 
-  // an exhausted cursor gets an empty buffer: its loads return zeros
+  // Buffer resources span the head's whole K or V buffer up to the end of the
+  // tile's segment: rows past the segment end read as zero, and an exhausted
+  // cursor gets an empty range (its loads return zeros).
   auto load_k = [&](const TileInfo& t) __attribute__((always_inline)) {
-    const uint32_t bytes = t.valid ? (uint32_t)((t.kv_len - 1) * kss + KROWB) : 0u;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (t.valid ? t.kv_row : 0) * kss), (short)0, (int)bytes,
-                                          0x00020000);
-    const int so = t.valid ? (int)(t.k0 * kss) : 0;
+    const uint32_t nrec = t.valid ? (uint32_t)(t.kv_row + t.kv_len - 1) * kss + ROWB : 0u;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, (int)nrec, 0x00020000);
+    const int so = (int)((uint32_t)(t.kv_row + t.k0) * kss);
     kst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff0, so, 0);
     kst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff1, so, 0);
   };
   auto load_v = [&](const TileInfo& t) __attribute__((always_inline)) {
-    const uint32_t bytes = t.valid ? (uint32_t)((t.kv_len - 1) * vss + KROWB) : 0u;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (t.valid ? t.kv_row : 0) * vss), (short)0, (int)bytes,
-                                          0x00020000);
-    const int so = t.valid ? (int)(t.k0 * vss) : 0;
+    const uint32_t nrec = t.valid ? (uint32_t)(t.kv_row + t.kv_len - 1) * vss + ROWB : 0u;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, (short)0, (int)nrec, 0x00020000);
+    const int so = (int)((uint32_t)(t.kv_row + t.k0) * vss);
     vst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff0, so, 0);
     vst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff1, so, 0);
   };
@@ -244,9 +306,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // Per-lane LDS offsets of the MFMA operands inside one tile buffer.  The
   // swizzle is an XOR with a per-lane value, so each distinct chunk gets its
   // own precomputed offset; buffer and block offsets fold into immediates.
-  int k_lane[8];  // K operand, 16-key step ks: row kperm(l32), chunk 2ks + g
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) k_lane[ks] = k_off(kperm(l32), 2 * ks + g);
+  const int k_lane = k_off(kperm(l32), g);  // K operand, 16-key step ks: + 32 ks
   // V^T operand of (dvb, b2, mm): row dvb*32 + l32, chunk c = 4b2 + 2mm + g.
   // vswz(dvb*32 + l32) = lsw ^ (2 dvb mod 8), so the stored chunk is
   // (x + g) ^ lsw with the even compile-time x = (4b2 + 2mm) ^ (2 dvb mod 8).
@@ -263,12 +323,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   bf16x8 pf[2][2];   // P^T of a tile, between its vector slot and its PV MFMAs:
                      // pf[b2][mm] holds tile keys b2*32 + 16mm + 8g + 0..7
   auto apply_mask = [&](const TileInfo& t) __attribute__((always_inline)) {
-    int64_t lim = (int64_t)t.kv_len - 1 - t.k0;
+    int lim = t.kv_len - 1 - t.k0;
     if (causal) {
-      const int64_t lc = (int64_t)my_p + t.delta - t.k0;
+      const int lc = my_p + t.delta - t.k0;
       lim = lc < lim ? lc : lim;
     }
-    const int lim32 = (lim < -1 ? -1 : (lim > 1000 ? 1000 : (int)lim)) - 8 * g;
+    const int lim32 = (lim < -1 ? -1 : (lim > 1000 ? 1000 : lim)) - 8 * g;
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
@@ -278,7 +338,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
   };
   auto tile_needs_mask = [&](const TileInfo& t) __attribute__((always_inline)) -> bool {
-    return (t.k0 + BN > t.kv_len) || (causal && (int64_t)(t.k0 + BN - 1) - p0 > t.delta);
+    return (t.k0 + BN > t.kv_len) || (causal && t.k0 + BN - 1 - p0 > t.delta);
   };
 
   // Vector work on a computed S^T: mask, maximum, reference update (rare O^T
@@ -334,7 +394,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     const unsigned char* kb = kbase + KB * KTILE;
     const unsigned char* vb = vbase + VB * VTILE;
     auto kread = [&](int i) __attribute__((always_inline)) {
-      return *(const bf16x8*)(kb + (i & 1) * 32 * KROWB + k_lane[i >> 1]);
+      return *(const bf16x8*)(kb + (i & 1) * 32 * KROWB + (i >> 1) * 32 + k_lane);
     };
     auto vread = [&](int i) __attribute__((always_inline)) {
       const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
@@ -368,17 +428,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   };
 
   // ---- tile stream: infos of tiles n-1 .. n+2 around loop iteration n
-  TileCursor<BN> cur = make_cursor<BN>(a, qg, wg_p_hi);
-  if (wg_p_hi < wg_p0) cur.done = true;
+  __syncthreads();  // run table complete
+  RunCursor cur;
+  cur.start(runs, wg_p_hi < wg_p0 ? 0 : nruns);
   auto next_info = [&]() __attribute__((always_inline)) -> TileInfo {
-    const TileInfo t = tile_info(cur);
-    if (!cur.done) cur.advance();
+    TileInfo t;
+    t.valid = !cur.done;
+    t.k0 = cur.k0;
+    t.kv_len = cur.kv_len;
+    t.delta = cur.delta;
+    t.kv_row = cur.kv_row;
+    if (!cur.done) cur.advance(runs);
     return t;
   };
   TileInfo tm1;  // tile n-1
   tm1.valid = false;
-  tm1.k0 = tm1.kv_len = tm1.delta = 0;
-  tm1.kv_row = 0;
+  tm1.k0 = tm1.kv_len = tm1.delta = tm1.kv_row = 0;
   TileInfo t0 = next_info();  // tile n
   TileInfo t1 = next_info();  // tile n+1
   TileInfo t2 = next_info();  // tile n+2

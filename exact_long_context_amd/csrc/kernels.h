@@ -12,6 +12,10 @@ namespace ra {
 // output finalized at the end (mode RING).
 enum FwdMode : int32_t { MODE_CHUNK = 0, MODE_RING = 1 };
 
+// The bf16 kernel keeps the table of the KV segments one workgroup walks in
+// LDS; a call may cover at most this many (ring steps x segments per chunk).
+constexpr int32_t BF16_MAX_RUNS = 1024;
+
 struct FwdArgs {
   const void* q;
   const void* k;

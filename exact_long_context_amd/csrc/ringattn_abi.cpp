@@ -132,12 +132,16 @@ ra_status plan_launch(ra::FwdArgs& a, bool bf16, int64_t seg_len, int32_t nseg_q
   return RA_OK;
 }
 
-// The bf16 kernel addresses one KV segment through a buffer resource with
-// 32-bit offsets.
-ra_status check_segment_bytes(const ra_attn_desc* d, int64_t kv_rows) {
+// The bf16 kernel addresses one head's K and V rows through buffer resources
+// with 32-bit byte offsets, and keeps the table of the KV segments it walks in
+// LDS (at most 1024 entries).
+ra_status check_kv_span(const ra_attn_desc* d, int64_t kv_rows, int64_t runs) {
+  if (d->in_dtype != RA_BF16) return RA_OK;
   const int64_t stride = (d->k.s > d->v.s ? d->k.s : d->v.s) * 2;
-  if (d->in_dtype == RA_BF16 && (kv_rows - 1) * stride + d->d * 2 > I32_MAX)
-    return fail(RA_ERR_UNSUPPORTED, "one KV segment spans more than 2 GiB (rows x row stride)");
+  if ((kv_rows - 1) * stride + d->d * 2 > I32_MAX)
+    return fail(RA_ERR_UNSUPPORTED, "one head's K or V rows span more than 2 GiB (rows x row stride)");
+  if (runs > ra::BF16_MAX_RUNS)
+    return fail(RA_ERR_UNSUPPORTED, "more than %d KV segments per call", (int)ra::BF16_MAX_RUNS);
   return RA_OK;
 }
 
@@ -206,7 +210,7 @@ ra_status ra_chunk_fwd(const ra_attn_desc* desc, const void* q, const void* k, c
   a.n_chunks = 1;
   a.q_count = 1;
   const bool bf16 = desc->in_dtype == RA_BF16;
-  if ((st = check_segment_bytes(desc, desc->lk)) != RA_OK) return st;
+  if ((st = check_kv_span(desc, desc->lk, 1)) != RA_OK) return st;
   if ((st = plan_launch(a, bf16, desc->lq, 1, 1)) != RA_OK) return st;
   // a causal offset below -(lq - 1) hides every key: nothing to do
   if (causal && causal_delta < -(desc->lq - 1)) return RA_OK;
@@ -269,7 +273,7 @@ ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, co
   a.lk = (int32_t)d->lk;
   const int32_t nseg = ra::num_segments(desc->layout);
   const bool bf16 = d->in_dtype == RA_BF16;
-  if ((st = check_segment_bytes(d, d->lk / nseg)) != RA_OK) return st;
+  if ((st = check_kv_span(d, desc->seq, (int64_t)desc->n_chunks * nseg)) != RA_OK) return st;
   if ((st = plan_launch(a, bf16, d->lq / nseg, nseg, desc->q_chunk_count)) != RA_OK) return st;
   return hip_status(bf16 ? ra::launch_attn_fwd_bf16(a, (hipStream_t)stream)
                          : ra::launch_attn_fwd_f32(a, (hipStream_t)stream),

@@ -39,7 +39,11 @@
  *   with d in {16, 32, 64, 128}; out_dtype F32 or BF16.  Other combinations
  *   return RA_ERR_UNSUPPORTED.  Device pointers must be 16-byte aligned and
  *   row strides (s) must be multiples of 8 elements for BF16 and of 4 for
- *   F32; the (b) and (h) strides likewise.
+ *   F32; the (b) and (h) strides likewise.  The BF16 path addresses one
+ *   head's K or V rows with 32-bit byte offsets and walks at most 1024 KV
+ *   segments per call (n_chunks for contiguous / striped, 2 n_chunks for
+ *   zig-zag): (kv rows - 1) x row stride + 2d must stay below 2^31 bytes, else
+ *   RA_ERR_UNSUPPORTED.
  */
 #ifndef RINGATTN_H
 #define RINGATTN_H

@@ -211,6 +211,15 @@ def test_ring_fwd_rejects_bad_descriptors(kw):
     assert _ring(**kw) == ra.RA_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("kw", [
+    dict(layout="zigzag", S=1026, N=513, count=1),       # 1026 KV segments
+    dict(layout="contiguous", S=2050, N=1025, count=1),  # 1025 KV segments
+    dict(layout="contiguous", S=256, N=4, k_s=1 << 24),  # K rows span 8 GiB
+])
+def test_ring_fwd_rejects_unsupported_bf16_extents(kw):
+    assert _ring(**kw) == ra.RA_ERR_UNSUPPORTED
+
+
 def test_ring_fwd_rejects_null_pointers_and_workspace():
     r = ra.ra_ring_desc()
     r.attn = _adesc(lq=64, lk=64)
