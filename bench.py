@@ -137,6 +137,46 @@ def traffic_record():
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_per_dispatch(csv_path, counter, name_part):
+    """Mean per-dispatch value of one rocprofv3 counter over the dispatches whose
+    kernel name contains name_part (values of one dispatch summed)."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{csv_path}: no {counter} rows for kernels matching '{name_part}'")
+    return sum(per.values()) / len(per), len(per)
+
+
+def write_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes=1 << 30):
+    """HBM bytes per launch of the attention kernel from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes, each scaled by what the same counter reads for a plain
+    device copy of copy_bytes (bench.py --copy-calib)."""
+    kib = 1024.0
+    f_attn, n1 = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "attn_fwd_bf16")
+    w_attn, n2 = _counter_per_dispatch(write_csv, "WRITE_SIZE", "attn_fwd_bf16")
+    f_copy, _ = _counter_per_dispatch(cfetch_csv, "FETCH_SIZE", "copyBuffer")
+    w_copy, _ = _counter_per_dispatch(cwrite_csv, "WRITE_SIZE", "copyBuffer")
+    rf = f_copy * kib / copy_bytes   # counter bytes per byte actually read
+    wf = w_copy * kib / copy_bytes
+    read_b = f_attn * kib / rf
+    write_b = w_attn * kib / wf
+    rec = {"kernel_sha256": hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest(),
+           "hbm_bytes_per_launch": read_b + write_b,
+           "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
+           "fetch_size_kib_per_launch": f_attn, "write_size_kib_per_launch": w_attn,
+           "copy_calibration": {"bytes": copy_bytes, "fetch_size_kib": f_copy, "write_size_kib": w_copy,
+                                "read_factor": rf, "write_factor": wf},
+           "dispatches": [n1, n2]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,7 +187,13 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain 1 GiB device copies (counter calibration) and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 counter CSVs into the traffic record under profiles/ and exit")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic), indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the ring runs over KV chunks resident in this GPU's HBM, "

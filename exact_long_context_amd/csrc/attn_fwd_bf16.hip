@@ -285,22 +285,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     *(u32x4*)(kb + k_off(kr, kc)) = kst[0];
     *(u32x4*)(kb + k_off(kr + 16, kc)) = kst[1];
   };
+  // V transpose: 2 keys x 8 dv -> 8 dv rows x 2 keys (4 bytes each).  Lanes
+  // with odd vc write the odd row of each pair first, which spreads every
+  // write instruction over all banks; the byte selector of v_perm_b32 picks
+  // the even or odd dv of the pair per lane.
+  const unsigned vsel[2] = {(vc & 1) ? 0x07060302u : 0x05040100u, (vc & 1) ? 0x05040100u : 0x07060302u};
   auto store_v = [&](unsigned char* vb) __attribute__((always_inline)) {
-    // 2 keys x 8 dv -> 8 dv rows x 2 keys (4 bytes each); lanes with odd vc
-    // write the odd row of each pair first, which spreads every write
-    // instruction over all banks
-    const bool odd = vc & 1;
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      const unsigned ev = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], 0x05040100u);
-      const unsigned od = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], 0x07060302u);
+    for (int pr = 0; pr < 4; ++pr)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int par = b ^ (int)odd;
-        const int dv = 8 * vc + 2 * pr + par;
-        *(unsigned*)(vb + v_off(dv, vk >> 2) + 4 * (vk & 3)) = par ? od : ev;
+        const int dv = 8 * vc + 2 * pr + (b ^ (vc & 1));
+        *(unsigned*)(vb + v_off(dv, vk >> 2) + 4 * (vk & 3)) = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], vsel[b]);
       }
-    }
   };
 
   // Per-lane LDS offsets of the MFMA operands inside one tile buffer.  The
