@@ -150,38 +150,67 @@ __device__ __forceinline__ Run make_run(const FwdArgs& a, const QGeom& qg, int32
   return e;
 }
 
-// Wave-uniform walk over the run table: tiles of BN keys in ring order.
-struct RunCursor {
-  int32_t ri, nruns, k0, kv_row, kv_len, delta, k_end;
-  bool done;
-  __device__ __forceinline__ void load(const Run* runs) {
-    const Run e = runs[ri];
-    kv_row = __builtin_amdgcn_readfirstlane(e.kv_row);
-    kv_len = __builtin_amdgcn_readfirstlane(e.kv_len);
-    delta = __builtin_amdgcn_readfirstlane(e.delta);
-    k_end = __builtin_amdgcn_readfirstlane(e.k_end);
-  }
-  __device__ __forceinline__ void skip_empty(const Run* runs) {
-    while (!done && k0 >= k_end) {
-      if (++ri >= nruns) { done = true; break; }
-      k0 = 0;
-      load(runs);
-    }
-  }
-  __device__ __forceinline__ void start(const Run* runs, int32_t n) {
-    nruns = n; ri = 0; k0 = 0; done = n <= 0;
-    kv_row = kv_len = delta = k_end = 0;
-    if (!done) { load(runs); skip_empty(runs); }
-  }
-  __device__ __forceinline__ void advance(const Run* runs) {
-    k0 += BN;
-    skip_empty(runs);
-  }
+// Scalar description of one tile of BN keys, produced by the cursor.
+struct TileInfo {
+  uint32_t meta;            // run index | need-mask bit 16 | valid bit 17
+  int32_t k0;               // first key of the tile inside its segment
+  uint32_t so_k, so_v;      // byte offset of the tile's first row in the head's K / V
+  uint32_t nrec_k, nrec_v;  // byte end of the segment in K / V (0 once exhausted)
+  __device__ __forceinline__ bool valid() const { return (meta >> 17) & 1; }
+  __device__ __forceinline__ bool need_mask() const { return (meta >> 16) & 1; }
+  __device__ __forceinline__ int run() const { return meta & 0xffff; }
 };
 
-struct TileInfo {
-  bool valid;
-  int32_t k0, kv_len, delta, kv_row;
+// Wave-uniform walk over the run table: tiles of BN keys in ring order.  A
+// tile advance is a few scalar adds; the per-run values (byte ranges of the
+// segment, the first key that needs a mask) are set up when a run starts.
+struct RunCursor {
+  int32_t ri, nruns, k0, k_end, thr;
+  uint32_t so_k, so_v, nrec_k, nrec_v;
+  bool done;
+  __device__ __forceinline__ void load(const Run* runs, uint32_t kss, uint32_t vss, int32_t p0, bool causal) {
+    const Run e = runs[ri];
+    const int32_t kv_row = __builtin_amdgcn_readfirstlane(e.kv_row);
+    const int32_t kv_len = __builtin_amdgcn_readfirstlane(e.kv_len);
+    const int32_t delta = __builtin_amdgcn_readfirstlane(e.delta);
+    k_end = __builtin_amdgcn_readfirstlane(e.k_end);
+    // a tile starting at k0 crosses the segment end when k0 > kv_len - BN and
+    // the diagonal of the wave's rows when k0 > delta + p0 - (BN - 1)
+    const int32_t t_end = kv_len - BN;
+    const int32_t t_diag = delta + p0 - (BN - 1);
+    thr = (causal && t_diag < t_end) ? t_diag : t_end;
+    so_k = (uint32_t)kv_row * kss;
+    so_v = (uint32_t)kv_row * vss;
+    nrec_k = (uint32_t)(kv_row + kv_len - 1) * kss + 2 * D;
+    nrec_v = (uint32_t)(kv_row + kv_len - 1) * vss + 2 * D;
+  }
+  __device__ __forceinline__ void skip_empty(const Run* runs, uint32_t kss, uint32_t vss, int32_t p0, bool causal) {
+    while (!done && k0 >= k_end) {
+      if (++ri >= nruns) { done = true; nrec_k = nrec_v = 0; break; }
+      k0 = 0;
+      load(runs, kss, vss, p0, causal);
+    }
+  }
+  __device__ __forceinline__ void start(const Run* runs, int32_t n, uint32_t kss, uint32_t vss, int32_t p0,
+                                        bool causal) {
+    nruns = n; ri = 0; k0 = 0; done = n <= 0;
+    k_end = thr = 0;
+    so_k = so_v = nrec_k = nrec_v = 0;
+    if (!done) { load(runs, kss, vss, p0, causal); skip_empty(runs, kss, vss, p0, causal); }
+  }
+  __device__ __forceinline__ TileInfo tile() const {
+    TileInfo t;
+    t.meta = (uint32_t)ri | ((k0 > thr ? 1u : 0u) << 16) | ((done ? 0u : 1u) << 17);
+    t.k0 = k0;
+    t.so_k = so_k; t.so_v = so_v; t.nrec_k = nrec_k; t.nrec_v = nrec_v;
+    return t;
+  }
+  __device__ __forceinline__ void advance(const Run* runs, uint32_t kss, uint32_t vss, int32_t p0, bool causal) {
+    k0 += BN;
+    so_k += BN * kss;
+    so_v += BN * vss;
+    skip_empty(runs, kss, vss, p0, causal);
+  }
 };
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int G = a.hq / a.hkv;
   const int h = it.kvh * G + it.hg * HP + (wave % HP);
   const int wg_p0 = it.tile * a.rows_per_wg;
-  const int p0 = wg_p0 + (wave / HP) * WAVE_ROWS;  // first row of this wave in the segment
+  const int p0 = __builtin_amdgcn_readfirstlane(wg_p0 + (wave / HP) * WAVE_ROWS);  // first row of this wave
   const int wg_p_hi = min(wg_p0 + a.rows_per_wg, qg.len) - 1;
   const int nruns = a.mode == MODE_CHUNK ? 1 : a.n_chunks * num_segments(a.layout);
   for (int r = tid; r < nruns; r += NTHREADS) runs[r] = make_run(a, qg, wg_p_hi, r);
@@ -268,18 +297,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // tile's segment: rows past the segment end read as zero, and an exhausted
   // cursor gets an empty range (its loads return zeros).
   auto load_k = [&](const TileInfo& t) __attribute__((always_inline)) {
-    const uint32_t nrec = t.valid ? (uint32_t)(t.kv_row + t.kv_len - 1) * kss + ROWB : 0u;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, (int)nrec, 0x00020000);
-    const int so = (int)((uint32_t)(t.kv_row + t.k0) * kss);
-    kst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff0, so, 0);
-    kst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff1, so, 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, (int)t.nrec_k, 0x00020000);
+    kst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff0, (int)t.so_k, 0);
+    kst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff1, (int)t.so_k, 0);
   };
   auto load_v = [&](const TileInfo& t) __attribute__((always_inline)) {
-    const uint32_t nrec = t.valid ? (uint32_t)(t.kv_row + t.kv_len - 1) * vss + ROWB : 0u;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, (short)0, (int)nrec, 0x00020000);
-    const int so = (int)((uint32_t)(t.kv_row + t.k0) * vss);
-    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff0, so, 0);
-    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff1, so, 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, (short)0, (int)t.nrec_v, 0x00020000);
+    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff0, (int)t.so_v, 0);
+    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff1, (int)t.so_v, 0);
   };
   auto store_k = [&](unsigned char* kb) __attribute__((always_inline)) {
     *(u32x4*)(kb + k_off(kr, kc)) = kst[0];
@@ -319,10 +344,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   f32x16 s[2];       // S^T of a tile, between its matrix slot and its vector slot
   bf16x8 pf[2][2];   // P^T of a tile, between its vector slot and its PV MFMAs:
                      // pf[b2][mm] holds tile keys b2*32 + 16mm + 8g + 0..7
+  // Masking (tiles that cross the diagonal or the segment end only): the
+  // run's length and causal offset come from the run table.
   auto apply_mask = [&](const TileInfo& t) __attribute__((always_inline)) {
-    int lim = t.kv_len - 1 - t.k0;
+    const Run e = runs[t.run()];
+    const int kv_len = __builtin_amdgcn_readfirstlane(e.kv_len);
+    const int delta = __builtin_amdgcn_readfirstlane(e.delta);
+    int lim = kv_len - 1 - t.k0;
     if (causal) {
-      const int lc = my_p + t.delta - t.k0;
+      const int lc = my_p + delta - t.k0;
       lim = lc < lim ? lc : lim;
     }
     const int lim32 = (lim < -1 ? -1 : (lim > 1000 ? 1000 : lim)) - 8 * g;
@@ -334,14 +364,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         s[b2][r] = kk > lim32 ? -INFINITY : s[b2][r];
       }
   };
-  auto tile_needs_mask = [&](const TileInfo& t) __attribute__((always_inline)) -> bool {
-    return (t.k0 + BN > t.kv_len) || (causal && t.k0 + BN - 1 - p0 > t.delta);
-  };
 
   // Vector work on a computed S^T: mask, maximum, reference update (rare O^T
   // rescale), exponentials into P^T and the row sum.
   auto softmax_tile = [&](const TileInfo& t) __attribute__((always_inline)) {
-    if (tile_needs_mask(t)) apply_mask(t);
+    if (t.need_mask()) apply_mask(t);
     // two chains of three-input maxima over the lane's 32 scores
     float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
@@ -427,28 +454,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // ---- tile stream: infos of tiles n-1 .. n+2 around loop iteration n
   __syncthreads();  // run table complete
   RunCursor cur;
-  cur.start(runs, wg_p_hi < wg_p0 ? 0 : nruns);
+  cur.start(runs, wg_p_hi < wg_p0 ? 0 : nruns, kss, vss, p0, causal);
   auto next_info = [&]() __attribute__((always_inline)) -> TileInfo {
-    TileInfo t;
-    t.valid = !cur.done;
-    t.k0 = cur.k0;
-    t.kv_len = cur.kv_len;
-    t.delta = cur.delta;
-    t.kv_row = cur.kv_row;
-    if (!cur.done) cur.advance(runs);
+    const TileInfo t = cur.tile();
+    if (!cur.done) cur.advance(runs, kss, vss, p0, causal);
     return t;
   };
-  TileInfo tm1;  // tile n-1
-  tm1.valid = false;
-  tm1.k0 = tm1.kv_len = tm1.delta = tm1.kv_row = 0;
-  TileInfo t0 = next_info();  // tile n
-  TileInfo t1 = next_info();  // tile n+1
-  TileInfo t2 = next_info();  // tile n+2
+  // ring of tile infos: around loop iteration n, ti[n % 4] is tile n and
+  // ti[(n + 3) % 4] tile n - 1 (the slot of tile n + 3 once it is produced)
+  TileInfo ti[4];
+  ti[3].meta = 0;  // tile -1: invalid
+  ti[3].k0 = 0;
+  ti[3].so_k = ti[3].so_v = ti[3].nrec_k = ti[3].nrec_v = 0;
+  ti[0] = next_info();
+  ti[1] = next_info();
+  ti[2] = next_info();
 
   // prologue: K(0) into K buffer 0 (both groups, one half each), V buffer 1
   // zeroed for the first PV, P^T zeroed; then the registers for the first
   // staging: K(1) and V(0)
-  load_k(t0);
+  load_k(ti[0]);
   store_k(kbase);
   *(u32x4*)(vbase + VTILE + tid * 32) = u32x4{0u, 0u, 0u, 0u};
   *(u32x4*)(vbase + VTILE + tid * 32 + 16) = u32x4{0u, 0u, 0u, 0u};
@@ -456,8 +481,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) pf[b2][mm] = bf16x8{};
-  load_k(t1);
-  load_v(t0);
+  load_k(ti[1]);
+  load_v(ti[0]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): retire every prologue load here
   __syncthreads();
 
@@ -466,40 +491,46 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   //   slot 2: A vector (softmax(n)), staging  |  B matrix (QK(n), PV(n-1))
   // Staging writes the group's halves of K(n+1) -> K buffer (n+1) % 2 and of
   // V(n) -> V buffer n % 2, then loads K(n+2) and V(n+1).
-  auto staging = [&](auto pc) __attribute__((always_inline)) {
-    constexpr int P = decltype(pc)::value;
-    store_k(kbase + (P ^ 1) * KTILE);
-    store_v(vbase + P * VTILE);
-    load_k(t2);
-    load_v(t1);
-  };
-  auto iteration = [&](auto pc) __attribute__((always_inline)) {
-    constexpr int P = decltype(pc)::value;   // n % 2
+  auto iteration = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;   // n % 4
+    constexpr int P = Q & 1;                 // n % 2
     const std::integral_constant<int, P> kbc{};
     const std::integral_constant<int, P ^ 1> vbc{};
+    const TileInfo& tm1 = ti[(Q + 3) & 3];
+    const TileInfo& t0 = ti[Q];
+    const TileInfo& t1 = ti[(Q + 1) & 3];
+    const TileInfo& t2 = ti[(Q + 2) & 3];
+    auto staging = [&]() __attribute__((always_inline)) {
+      store_k(kbase + (P ^ 1) * KTILE);
+      store_v(vbase + P * VTILE);
+      load_k(t2);
+      load_v(t1);
+    };
     if (grp == 0) {
       matrix_slot(kbc, vbc);
     } else {
-      if (tm1.valid) softmax_tile(tm1);
-      staging(pc);
+      if (tm1.valid()) softmax_tile(tm1);
+      staging();
     }
     __syncthreads();
     if (grp == 0) {
-      if (t0.valid) softmax_tile(t0);
-      staging(pc);
+      if (t0.valid()) softmax_tile(t0);
+      staging();
     } else {
       matrix_slot(kbc, vbc);
     }
     __syncthreads();
-    tm1 = t0;
-    t0 = t1;
-    t1 = t2;
-    t2 = next_info();
+    ti[(Q + 3) & 3] = next_info();  // tile n + 3 takes the place of tile n - 1
   };
-  while (t0.valid || tm1.valid) {
+  for (;;) {
+    if (!(ti[0].valid() || ti[3].valid())) break;
     iteration(std::integral_constant<int, 0>{});
-    if (!(t0.valid || tm1.valid)) break;
+    if (!(ti[1].valid() || ti[0].valid())) break;
     iteration(std::integral_constant<int, 1>{});
+    if (!(ti[2].valid() || ti[1].valid())) break;
+    iteration(std::integral_constant<int, 2>{});
+    if (!(ti[3].valid() || ti[2].valid())) break;
+    iteration(std::integral_constant<int, 3>{});
   }
 
   // ---- epilogue
