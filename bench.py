@@ -87,6 +87,46 @@ def time_workload(w, steps, warmup, api, torch):
     return ms, wall
 
 
+def balance_report(w, api, torch):
+    """Per-query-chunk work of a causal workload in its own layout and in the
+    contiguous layout at the same shape: visible pairs from the schedule and the
+    measured time of each query chunk computed alone (one device's share)."""
+    import synthetic
+    from exact_long_context_amd import ringattn as ra
+    q, k, v = synthetic.draw(w, device="cuda")
+    rep = {}
+    for layout in (w.layout, "contiguous"):
+        qp = api.to_chunked(q, layout, w.n_chunks)
+        kp = api.to_chunked(k, layout, w.n_chunks)
+        vp = api.to_chunked(v, layout, w.n_chunks)
+        L = w.chunk
+        pairs, ms = [], []
+        for i in range(w.n_chunks):
+            qi = qp[:, :, i * L:(i + 1) * L].contiguous()
+            out = torch.empty(qi.shape, dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty(qi.shape[:3], dtype=torch.float32, device="cuda")
+            desc = ra.ring_desc(qi, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=layout, causal=w.causal,
+                                q_chunk_first=i, out=out, lse=lse)
+            pairs.append(visible_pairs(ra.ra_ring_schedule(desc, i)))
+            stream = torch.cuda.current_stream()
+            ra.ra_ring_fwd(desc, qi, kp, vp, out, lse, stream=stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(3):
+                ra.ra_ring_fwd(desc, qi, kp, vp, out, lse, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1) / 3)
+        rep[layout] = {"visible_pairs_max_over_min": round(max(pairs) / min(pairs), 6),
+                       "visible_pairs_max_over_mean": round(max(pairs) / (sum(pairs) / len(pairs)), 6),
+                       "ms_max_over_min": round(max(ms) / min(ms), 3),
+                       "ms_per_query_chunk": [round(x, 3) for x in ms]}
+        del qp, kp, vp
+        torch.cuda.empty_cache()
+    return rep
+
+
 def cpu_baseline(w, flop_total):
     """The float64 oracle as it stands, on a bounded sample of the workload's
     query rows (one KV head's query heads, early and late rows), scaled to the
@@ -231,6 +271,12 @@ def main():
             others[name] = {"ms": round(mo, 4), "tflops": round(fo / (mo * 1e-3) / 1e12, 2)}
             log(f"  {name}: {mo:.3f} ms  {others[name]['tflops']} TFLOP/s")
             torch.cuda.empty_cache()
+            if name == "causal_striped_128k":
+                others[name]["per_query_chunk_balance"] = balance_report(wo, api, torch)
+                for lay, r in others[name]["per_query_chunk_balance"].items():
+                    log(f"    {lay}: visible pairs max/min {r['visible_pairs_max_over_min']}, "
+                        f"time max/min {r['ms_max_over_min']}")
+                torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

@@ -88,6 +88,8 @@ SMALL = [
     ("contiguous", 256, 1, 2, 2, 1, True),     # one chunk
     ("zigzag", 64, 32, 2, 2, 1, True),         # L = 2, s = 1
     ("striped", 64, 64, 2, 1, 1, True),        # L = 1
+    ("zigzag", 1024, 512, 2, 1, 1, True),      # 1024 KV segments: the largest run table
+    ("contiguous", 1024, 1024, 2, 2, 1, True),  # 1024 chunks of one token
 ]
 
 
