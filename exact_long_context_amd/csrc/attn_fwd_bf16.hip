@@ -27,13 +27,14 @@
 // barriers, with group B one slot behind group A:
 //   matrix slot : S^T of tile n and O^T += V^T P^T of tile n-1 (32 MFMA,
 //                 operand reads issued ahead of use)
-//   vector slot : mask / max / exponentials of the tile whose S^T it holds,
-//                 plus the group's half of the K / V staging (LDS writes,
-//                 global loads one iteration ahead)
+//   vector slot : mask / max / exponentials / row sum of the tile whose S^T
+//                 it holds
 // so while one wave of a SIMD runs its matrix slot the other runs its vector
-// slot, and the matrix core and the vector ALU work at the same time.
-// Iteration n stages K(n+1) into K buffer (n+1) % 2 and V(n) into V buffer
-// n % 2 (64 KiB of LDS in all).
+// slot, and the matrix core and the vector ALU work at the same time.  The
+// group's half of the K / V staging (LDS writes, global loads one iteration
+// ahead) follows its MFMAs in the matrix slot.  Iteration n stages K(n+1)
+// into K buffer (n+1) % 2 and V(n) into V buffer n % 2 (66 KiB of LDS for
+// the tiles, 16 KiB for the run table).
 //
 // Layout tricks:
 //   * S is computed transposed (keys x queries): one query per lane, 32 keys
@@ -432,6 +433,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       kq[i] = kread(i);
       vq[i] = vread(i);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the first reads go out before anything else
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
@@ -487,10 +489,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   __syncthreads();
 
   // Loop iteration n (two slots, a barrier after each):
-  //   slot 1: A matrix (QK(n), PV(n-1))  |  B vector (softmax(n-1)), staging
-  //   slot 2: A vector (softmax(n)), staging  |  B matrix (QK(n), PV(n-1))
+  //   slot 1: A matrix (QK(n), PV(n-1)), staging  |  B vector (softmax(n-1))
+  //   slot 2: A vector (softmax(n))  |  B matrix (QK(n), PV(n-1)), staging
   // Staging writes the group's halves of K(n+1) -> K buffer (n+1) % 2 and of
-  // V(n) -> V buffer n % 2, then loads K(n+2) and V(n+1).
+  // V(n) -> V buffer n % 2, then loads K(n+2) and V(n+1).  It follows the
+  // group's MFMAs, whose tail it overlaps, and reads or writes no buffer that
+  // the other group uses in the same slot.
   auto iteration = [&](auto qc) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;   // n % 4
     constexpr int P = Q & 1;                 // n % 2
@@ -508,16 +512,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     };
     if (grp == 0) {
       matrix_slot(kbc, vbc);
+      staging();
     } else {
       if (tm1.valid()) softmax_tile(tm1);
-      staging();
     }
     __syncthreads();
     if (grp == 0) {
       if (t0.valid()) softmax_tile(t0);
-      staging();
     } else {
       matrix_slot(kbc, vbc);
+      staging();
     }
     __syncthreads();
     ti[(Q + 3) & 3] = next_info();  // tile n + 3 takes the place of tile n - 1
