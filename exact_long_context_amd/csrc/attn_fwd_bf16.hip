@@ -32,7 +32,7 @@
 // so while one wave of a SIMD runs its matrix slot the other runs its vector
 // slot, and the matrix core and the vector ALU work at the same time.  The
 // group's half of the K / V staging (LDS writes, global loads one iteration
-// ahead) follows its MFMAs in the matrix slot.  Iteration n stages K(n+1)
+// ahead) runs between the last MFMAs of its matrix slot.  Iteration n stages K(n+1)
 // into K buffer (n+1) % 2 and V(n) into V buffer n % 2 (66 KiB of LDS for
 // the tiles, 16 KiB for the run table).
 //
@@ -316,14 +316,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // write instruction over all banks; the byte selector of v_perm_b32 picks
   // the even or odd dv of the pair per lane.
   const unsigned vsel[2] = {(vc & 1) ? 0x07060302u : 0x05040100u, (vc & 1) ? 0x05040100u : 0x07060302u};
-  auto store_v = [&](unsigned char* vb) __attribute__((always_inline)) {
+  auto store_v_pair = [&](unsigned char* vb, int pr) __attribute__((always_inline)) {
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int dv = 8 * vc + 2 * pr + (b ^ (vc & 1));
-        *(unsigned*)(vb + v_off(dv, vk >> 2) + 4 * (vk & 3)) = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], vsel[b]);
-      }
+    for (int b = 0; b < 2; ++b) {
+      const int dv = 8 * vc + 2 * pr + (b ^ (vc & 1));
+      *(unsigned*)(vb + v_off(dv, vk >> 2) + 4 * (vk & 3)) = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], vsel[b]);
+    }
   };
 
   // Per-lane LDS offsets of the MFMA operands inside one tile buffer.  The
@@ -414,7 +412,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // read has time to land.  At the ends of the stream one half works on stale
   // or zero data: a QK with no tile behind it is never used, and the first PV
   // multiplies P^T = 0 with a zeroed V buffer.
-  auto matrix_slot = [&](auto kbc, auto vbc) __attribute__((always_inline)) {
+  auto matrix_slot = [&](auto kbc, auto vbc, auto side) __attribute__((always_inline)) {
     constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
     const unsigned char* kb = kbase + KB * KTILE;
     const unsigned char* vb = vbase + VB * VTILE;
@@ -449,6 +447,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       s[b2] = mfma(kf, qf[ks], s[b2]);
       const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
       acc[dvb] = mfma(vf, pf[pb2][pmm], acc[dvb]);
+      __builtin_amdgcn_sched_barrier(0);
+      side(i);  // staging work placed between the last MFMA pairs
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -492,9 +492,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   //   slot 1: A matrix (QK(n), PV(n-1)), staging  |  B vector (softmax(n-1))
   //   slot 2: A vector (softmax(n))  |  B matrix (QK(n), PV(n-1)), staging
   // Staging writes the group's halves of K(n+1) -> K buffer (n+1) % 2 and of
-  // V(n) -> V buffer n % 2, then loads K(n+2) and V(n+1).  It follows the
-  // group's MFMAs, whose tail it overlaps, and reads or writes no buffer that
-  // the other group uses in the same slot.
+  // V(n) -> V buffer n % 2, then loads K(n+2) and V(n+1).  It runs between
+  // the group's last MFMAs and touches no buffer that either group reads in
+  // the same slot.
   auto iteration = [&](auto qc) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;   // n % 4
     constexpr int P = Q & 1;                 // n % 2
@@ -504,15 +504,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     const TileInfo& t0 = ti[Q];
     const TileInfo& t1 = ti[(Q + 1) & 3];
     const TileInfo& t2 = ti[(Q + 2) & 3];
-    auto staging = [&]() __attribute__((always_inline)) {
-      store_k(kbase + (P ^ 1) * KTILE);
-      store_v(vbase + P * VTILE);
-      load_k(t2);
-      load_v(t1);
+    // the group's staging, spread over the last four MFMA pairs of its
+    // matrix slot: K(n+1) and V(n) into LDS, then the loads of K(n+2), V(n+1)
+    auto staging = [&](int i) __attribute__((always_inline)) {
+      unsigned char* kdst = kbase + (P ^ 1) * KTILE;
+      unsigned char* vdst = vbase + P * VTILE;
+      if (i == 12) { store_k(kdst); store_v_pair(vdst, 0); }
+      if (i == 13) { store_v_pair(vdst, 1); store_v_pair(vdst, 2); }
+      if (i == 14) store_v_pair(vdst, 3);
+      if (i == 15) { load_k(t2); load_v(t1); }
     };
     if (grp == 0) {
-      matrix_slot(kbc, vbc);
-      staging();
+      matrix_slot(kbc, vbc, staging);
     } else {
       if (tm1.valid()) softmax_tile(tm1);
     }
@@ -520,8 +523,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     if (grp == 0) {
       if (t0.valid()) softmax_tile(t0);
     } else {
-      matrix_slot(kbc, vbc);
-      staging();
+      matrix_slot(kbc, vbc, staging);
     }
     __syncthreads();
     ti[(Q + 3) & 3] = next_info();  // tile n + 3 takes the place of tile n - 1
