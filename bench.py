@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain 1 GiB device copies (counter calibration) and exit")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the sustained bf16 MFMA rate (zero and random operands) and exit")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 counter CSVs into the traffic record under profiles/ and exit")
     args = ap.parse_args()
@@ -244,6 +246,21 @@ def main():
     import synthetic
     from exact_long_context_amd import api
     from exact_long_context_amd import ringattn as ra
+
+    if args.mfma_ceiling:
+        import ctypes
+        lib = ctypes.CDLL(os.path.join(ROOT, "exact_long_context_amd", "libramfmaprobe.so"))
+        lib.ra_probe_mfma_bf16.restype = ctypes.c_int
+        res = {}
+        for name, rnd in (("zero_operands", 0), ("random_operands", 1)):
+            ms, tf, ghz = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+            rc = lib.ra_probe_mfma_bf16(2048, 16000, rnd, ctypes.byref(ms), ctypes.byref(tf), ctypes.byref(ghz))
+            if rc != 0:
+                raise SystemExit(f"MFMA probe failed with HIP error {rc}")
+            res[name] = {"ms": round(ms.value, 3), "tflops": round(tf.value, 1), "clock_ghz": round(ghz.value, 3),
+                         "frac_of_peak": round(tf.value / PEAK_BF16_TFLOPS, 4)}
+        print(json.dumps({"v_mfma_f32_32x32x16_bf16_sustained": res}))
+        return
 
     if args.copy_calib:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
