@@ -30,11 +30,11 @@
 //   vector slot : mask / max / exponentials / row sum of the tile whose S^T
 //                 it holds
 // so while one wave of a SIMD runs its matrix slot the other runs its vector
-// slot, and the matrix core and the vector ALU work at the same time.  The
-// group's half of the K / V staging (LDS writes, global loads one iteration
-// ahead) runs between the last MFMAs of its matrix slot.  Iteration n stages K(n+1)
-// into K buffer (n+1) % 2 and V(n) into V buffer n % 2 (66 KiB of LDS for
-// the tiles, 16 KiB for the run table).
+// slot, and the matrix core and the vector ALU work at the same time.
+// Staging: buffer loads that write LDS directly (no registers, no LDS store
+// instructions); iteration n fills K buffer (n+1) % 2 with K(n+1) and V buffer
+// n % 2 with V(n), issued at the start of the iteration and waited for at its
+// end (64 KiB of LDS for the tiles, 16 KiB for the run table).
 //
 // Layout tricks:
 //   * S is computed transposed (keys x queries): one query per lane, 32 keys
@@ -42,9 +42,9 @@
 //     row sum needs no exchange until the end.
 //   * The K rows fed to the QK MFMA are permuted (bits 2 and 3 of the row index
 //     swapped) so that the 8 keys a lane holds per PV MFMA are 8 consecutive
-//     keys; the V^T operand is then one 16-byte LDS read.
-//   * V is transposed while it is staged (2 keys x 8 dv register transposes
-//     with v_perm_b32), so both MFMA operands come from ds_read_b128.
+//     keys.
+//   * V stays row-major in LDS; the V^T operand comes from transposing LDS
+//     reads (ds_read_b64_tr_b16), so V needs no register transposes.
 //   * K and V load through buffer resources bounded by the KV segment: rows
 //     past the segment end read as zero, with no per-row branches.
 #include <hip/hip_runtime.h>
@@ -63,34 +63,35 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 128;
 constexpr int BN = 64;           // keys per tile
 constexpr int WAVE_ROWS = 32;    // query rows per wave
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int ROWB = D * 2;        // bytes of one K or V row in global memory
-constexpr int KROWB = ROWB + 16;   // LDS pitch of one K row (16 bytes of padding)
-constexpr int VROWB = BN * 2;      // bytes of one V^T row (64 keys) in LDS
-constexpr int KTILE = BN * KROWB;  // 17 KiB
-constexpr int VTILE = D * VROWB;   // 16 KiB
+constexpr int ROWB = D * 2;        // bytes of one K or V row
+constexpr int KTILE = BN * ROWB;   // 16 KiB
+constexpr int VTILE = BN * ROWB;   // 16 KiB
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
-// K tile: row-major with a padded pitch of 272 bytes.  A K operand read
-// touches 16 distinct rows at one 16-byte chunk; the pitch moves each row by
-// four banks, so the read covers every bank once, and the addresses of the
-// eight 16-key steps differ by constants (one base register per lane).
-__device__ __forceinline__ int k_off(int row, int chunk) { return row * KROWB + (chunk << 4); }
-// V^T tile: row dv holds 64 keys (8 chunks of 16 B); chunk c of row dv is
-// stored at c ^ vswz(dv).  A V operand read touches 16 consecutive dv rows
-// (aligned to 16) at one chunk, where vswz takes 8 distinct values on each
-// parity class; a staging write touches rows 8vc + j for 16 values of vc,
-// where (parity, vswz) is made distinct by the write order below.  Both are
-// then free of bank conflicts.
-__device__ __forceinline__ int vswz(int dv) { return ((dv >> 1) ^ (dv >> 4)) & 7; }
-__device__ __forceinline__ int v_off(int dv, int chunk) { return dv * VROWB + ((chunk ^ vswz(dv)) << 4); }
+// K tile in LDS: blocks of 16 rows; inside a block, 16-byte chunk c of all 16
+// rows comes before chunk c + 1.  A K operand read (16 rows at one chunk per
+// 16 lanes) then covers 256 contiguous bytes, and the 16-key steps of a read
+// sequence differ by constants.  A 1 KiB staging block holds 4 chunks of 16
+// rows (64 bytes of each global row).
+__device__ __forceinline__ int k_pos(int row, int chunk) { return (row >> 4) * 4096 + chunk * 256 + (row & 15) * 16; }
+// V tile in LDS: row-major (one 256-byte row per key), 16-byte chunk c of key
+// row r stored at c ^ 4 (r % 4).  The V^T operand comes from two transposing
+// reads (ds_read_b64_tr_b16), each over 4 consecutive keys x 16 dv per
+// 16 lanes; the swizzle puts the four 64-byte pieces of those keys on
+// different banks.  Staging writes whole rows.
+__device__ __forceinline__ int v_pos(int key, int chunk) { return key * ROWB + ((chunk ^ ((key & 3) << 2)) << 4); }
 // Row of the K tile that feeds MFMA row i of a 32-key block.
 __device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
@@ -215,10 +216,13 @@ struct RunCursor {
 };
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * KTILE + 2 * VTILE];
+  // four distinct arrays, so that the compiler can tell the buffer being
+  // filled from the one being read and inserts no wait between them
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[KTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[KTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[VTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[VTILE];
   __shared__ Run runs[MAX_RUNS];
-  unsigned char* const kbase = smem;
-  unsigned char* const vbase = smem + 2 * KTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -281,61 +285,63 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const bool causal = a.causal != 0;
 
   // ---- staging: each group moves its half of every tile (keys 32 grp ..
-  // 32 grp + 31).  Buffer loads relative to the tile's KV segment; rows past
-  // the segment end are out of range and read as zero (masked keys must meet
-  // finite V), so no bounds branches are needed.
-  // K: thread -> 16-byte chunk kc of rows kr and kr + 16
-  const int kc = gtid & 15;
-  const int kr = 32 * grp + (gtid >> 4);
-  const uint32_t koff0 = kr * kss + kc * 16, koff1 = (kr + 16) * kss + kc * 16;
-  // V: thread -> dv chunk vc (dv 8vc .. 8vc+7) and key pair vk (keys 2vk, 2vk+1)
-  const int vc = gtid & 15;
-  const int vk = 16 * grp + (gtid >> 4);
-  const uint32_t voff0 = 2 * vk * vss + vc * 16, voff1 = (2 * vk + 1) * vss + vc * 16;
-  u32x4 kst[2], vst[2];
+  // 32 grp + 31) with buffer loads that write LDS directly (16 bytes per lane,
+  // lane l to byte 16 l of a 1 KiB block).  Loads are relative to the tile's
+  // KV segment; rows past the segment end are out of range and arrive as
+  // zeros (masked keys must meet finite V), so no bounds branches are needed.
+  const int wv = __builtin_amdgcn_readfirstlane(wave & 3);  // wave inside the group
+  // K: wave wv fills row block 2 grp + wv / 2, chunks 8 (wv % 2) .. + 7
+  const int k_rb = 2 * grp + (wv >> 1);
+  int k_dst[2];
+  uint32_t k_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = 2 * (wv & 1) + i;  // 1 KiB block inside the row block: chunks 4 blk .. 4 blk + 3
+    k_dst[i] = __builtin_amdgcn_readfirstlane(k_rb * 4096 + blk * 1024);
+    k_src[i] = (uint32_t)(16 * k_rb + (lane & 15)) * kss + (uint32_t)(4 * blk + (lane >> 4)) * 16;
+  }
+  // V: wave wv fills key rows 32 grp + 8 wv .. + 7, four rows per block; the
+  // lane that lands on stored chunk lane % 16 of row r fetches chunk
+  // (lane % 16) ^ 4 (r % 4), with r % 4 = lane / 16
+  int v_dst[2];
+  uint32_t v_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r0 = 32 * grp + 8 * wv + 4 * i;
+    v_dst[i] = __builtin_amdgcn_readfirstlane(r0 * ROWB);
+    v_src[i] = (uint32_t)(r0 + (lane >> 4)) * vss + (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) << 4);
+  }
 
   // Buffer resources span the head's whole K or V buffer up to the end of the
   // tile's segment: rows past the segment end read as zero, and an exhausted
-  // cursor gets an empty range (its loads return zeros).
-  auto load_k = [&](const TileInfo& t) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, (int)t.nrec_k, 0x00020000);
-    kst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff0, (int)t.so_k, 0);
-    kst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff1, (int)t.so_k, 0);
-  };
-  auto load_v = [&](const TileInfo& t) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, (short)0, (int)t.nrec_v, 0x00020000);
-    vst[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff0, (int)t.so_v, 0);
-    vst[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff1, (int)t.so_v, 0);
-  };
-  auto store_k = [&](unsigned char* kb) __attribute__((always_inline)) {
-    *(u32x4*)(kb + k_off(kr, kc)) = kst[0];
-    *(u32x4*)(kb + k_off(kr + 16, kc)) = kst[1];
-  };
-  // V transpose: 2 keys x 8 dv -> 8 dv rows x 2 keys (4 bytes each).  Lanes
-  // with odd vc write the odd row of each pair first, which spreads every
-  // write instruction over all banks; the byte selector of v_perm_b32 picks
-  // the even or odd dv of the pair per lane.
-  const unsigned vsel[2] = {(vc & 1) ? 0x07060302u : 0x05040100u, (vc & 1) ? 0x05040100u : 0x07060302u};
-  auto store_v_pair = [&](unsigned char* vb, int pr) __attribute__((always_inline)) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int dv = 8 * vc + 2 * pr + (b ^ (vc & 1));
-      *(unsigned*)(vb + v_off(dv, vk >> 2) + 4 * (vk & 3)) = __builtin_amdgcn_perm(vst[1][pr], vst[0][pr], vsel[b]);
+  // cursor gets an empty range (its loads write zeros).
+  // one 1 KiB block: j = 0, 1 K blocks of tile tk, j = 2, 3 V blocks of tile tv
+  auto stage_block = [&](int j, const TileInfo& tk, unsigned char* kb, const TileInfo& tv, unsigned char* vb)
+      __attribute__((always_inline)) {
+    if (j < 2) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, (int)tk.nrec_k, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kb + k_dst[j]), 16, k_src[j], (int)tk.so_k, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, (short)0, (int)tv.nrec_v, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(vb + v_dst[j - 2]), 16, v_src[j - 2], (int)tv.so_v, 0, 0);
     }
   };
 
-  // Per-lane LDS offsets of the MFMA operands inside one tile buffer.  The
-  // swizzle is an XOR with a per-lane value, so each distinct chunk gets its
-  // own precomputed offset; buffer and block offsets fold into immediates.
-  const int k_lane = k_off(kperm(l32), g);  // K operand, 16-key step ks: + 32 ks
-  // V^T operand of (dvb, b2, mm): row dvb*32 + l32, chunk c = 4b2 + 2mm + g.
-  // vswz(dvb*32 + l32) = lsw ^ (2 dvb mod 8), so the stored chunk is
-  // (x + g) ^ lsw with the even compile-time x = (4b2 + 2mm) ^ (2 dvb mod 8).
+  // Per-lane LDS offsets of the MFMA operands inside one tile buffer; the
+  // steps of a slot add compile-time constants.
+  // K operand of (b2, ks): rows kperm(l32) + 32 b2, chunk 2 ks + g
+  const int k_lane = k_pos(kperm(l32), g);  // + 8192 b2 + 512 ks
+  // V^T operand of (dvb, b2, mm): dv = 32 dvb + l32, keys 32 b2 + 16 mm + 8 g
+  // + 0..7, as two transposing reads of 4 keys.  In a read, lane 16 G + j
+  // (j < 16) addresses key row (4 keys) + j / 4 at dv 32 dvb + 16 (G % 2) +
+  // 4 (j % 4); the transpose hands lane 16 G + j the 4 keys of dv
+  // 32 dvb + 16 (G % 2) + j.
   int v_lane[4];
   {
-    const int lsw = ((l32 >> 1) & 7) ^ (l32 >> 4);
+    const int G = lane >> 4, j = lane & 15, q = j >> 2;
 #pragma unroll
-    for (int xh = 0; xh < 4; ++xh) v_lane[xh] = l32 * VROWB + (((2 * xh + g) ^ lsw) << 4);
+    for (int dvb = 0; dvb < 4; ++dvb)
+      v_lane[dvb] = (8 * g + q) * ROWB + ((((dvb ^ q) << 2) + 2 * (G & 1) + ((j & 3) >> 1)) << 4) + (j & 1) * 8;
   }
 
   // Mask a tile: register r of block b2 in half-wave g is tile key
@@ -366,7 +372,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   // Vector work on a computed S^T: mask, maximum, reference update (rare O^T
   // rescale), exponentials into P^T and the row sum.
-  auto softmax_tile = [&](const TileInfo& t) __attribute__((always_inline)) {
+  // side(j), j = 0..3, is called at four points spread over the slot
+  auto softmax_tile = [&](const TileInfo& t, auto side) __attribute__((always_inline)) {
+    side(0);
     if (t.need_mask()) apply_mask(t);
     // two chains of three-input maxima over the lane's 32 scores
     float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
@@ -387,6 +395,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] *= alpha;
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    side(1);
     // The row sum adds the fp32 exponentials (four chains).  It is not taken
     // with v_dot2 over the bf16 pairs: dot instructions wait for the matrix
     // core, which the other wave of the SIMD keeps busy during this slot.
@@ -403,8 +412,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
           pf[b2][mm][e + 1] = (__bf16)p1;
           float& r = rs[2 * b2 + mm];
           r = e == 0 ? p0 + p1 : (r + p0) + p1;
+          if (b2 == 0 && mm == 1 && e == 6) side(2);
         }
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    side(3);
   };
 
   // Matrix slot: S^T of the tile in K buffer KB and O^T += V^T P^T with the
@@ -414,15 +425,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // multiplies P^T = 0 with a zeroed V buffer.
   auto matrix_slot = [&](auto kbc, auto vbc, auto side) __attribute__((always_inline)) {
     constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
-    const unsigned char* kb = kbase + KB * KTILE;
-    const unsigned char* vb = vbase + VB * VTILE;
+    const unsigned char* kb = KB ? kbuf1 : kbuf0;
+    const unsigned char* vb = VB ? vbuf1 : vbuf0;
     auto kread = [&](int i) __attribute__((always_inline)) {
-      return *(const bf16x8*)(kb + (i & 1) * 32 * KROWB + (i >> 1) * 32 + k_lane);
+      return *(const bf16x8*)(kb + k_lane + (i & 1) * 8192 + (i >> 1) * 512);
     };
     auto vread = [&](int i) __attribute__((always_inline)) {
       const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
-      const int x = (4 * pb2 + 2 * pmm) ^ ((2 * dvb) & 7);
-      return *(const bf16x8*)(vb + dvb * 32 * VROWB + v_lane[x >> 1]);
+      const unsigned char* p = vb + v_lane[dvb] + (32 * pb2 + 16 * pmm) * ROWB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
+      const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, w);
     };
     constexpr int AHEAD = 2;  // operand reads in flight per chain
     bf16x8 kq[AHEAD], vq[AHEAD];
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
       acc[dvb] = mfma(vf, pf[pb2][pmm], acc[dvb]);
       __builtin_amdgcn_sched_barrier(0);
-      side(i);  // staging work placed between the last MFMA pairs
+      side(i);  // staging issue placed between MFMA pairs
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -472,29 +486,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   ti[1] = next_info();
   ti[2] = next_info();
 
-  // prologue: K(0) into K buffer 0 (both groups, one half each), V buffer 1
-  // zeroed for the first PV, P^T zeroed; then the registers for the first
-  // staging: K(1) and V(0)
-  load_k(ti[0]);
-  store_k(kbase);
-  *(u32x4*)(vbase + VTILE + tid * 32) = u32x4{0u, 0u, 0u, 0u};
-  *(u32x4*)(vbase + VTILE + tid * 32 + 16) = u32x4{0u, 0u, 0u, 0u};
+  // prologue: K(0) into K buffer 0 (both groups, one half each), both V
+  // buffers zeroed (the first PV multiplies P^T = 0 with V buffer 1, and every
+  // later V byte is finite tile data), P^T zeroed, S^T = -inf (tile -1)
+  stage_block(0, ti[0], kbuf0, ti[0], vbuf0);
+  stage_block(1, ti[0], kbuf0, ti[0], vbuf0);
 #pragma unroll
-  for (int b2 = 0; b2 < 2; ++b2)
+  for (int c = 0; c < 2; ++c) {
+    *(u32x4*)(vbuf0 + tid * 32 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(vbuf1 + tid * 32 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2) {
+    s[b2] = f32x16{} - INFINITY;
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) pf[b2][mm] = bf16x8{};
-  load_k(ti[1]);
-  load_v(ti[0]);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): retire every prologue load here
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(0) is in LDS
   __syncthreads();
 
+  // Barrier between slots.  Not __syncthreads(): its release fence would wait
+  // for the staging loads in flight (they write LDS); the staging is waited
+  // for explicitly before the second barrier of an iteration instead.  LDS
+  // reads have all been consumed by the end of a slot; the wait on them is
+  // kept for form's sake.
+  auto slot_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
   // Loop iteration n (two slots, a barrier after each):
-  //   slot 1: A matrix (QK(n), PV(n-1)), staging  |  B vector (softmax(n-1))
-  //   slot 2: A vector (softmax(n))  |  B matrix (QK(n), PV(n-1)), staging
-  // Staging writes the group's halves of K(n+1) -> K buffer (n+1) % 2 and of
-  // V(n) -> V buffer n % 2, then loads K(n+2) and V(n+1).  It runs between
-  // the group's last MFMAs and touches no buffer that either group reads in
-  // the same slot.
+  //   slot 1: A matrix (QK(n), PV(n-1))  |  B vector (softmax(n-1))
+  //   slot 2: A vector (softmax(n))  |  B matrix (QK(n), PV(n-1))
+  // Staging of K(n+1) into K buffer (n+1) % 2 and of V(n) into V buffer n % 2
+  // is issued in slot 1 by both groups, one 1 KiB block per wave at a time
+  // (group A between its first MFMA pairs, group B spread over its softmax),
+  // and waited for at the end of slot 2; neither buffer is read in iteration n.
   auto iteration = [&](auto qc) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;   // n % 4
     constexpr int P = Q & 1;                 // n % 2
@@ -503,32 +532,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     const TileInfo& tm1 = ti[(Q + 3) & 3];
     const TileInfo& t0 = ti[Q];
     const TileInfo& t1 = ti[(Q + 1) & 3];
-    const TileInfo& t2 = ti[(Q + 2) & 3];
-    // the group's staging, spread over the last four MFMA pairs of its
-    // matrix slot: K(n+1) and V(n) into LDS, then the loads of K(n+2), V(n+1)
-    auto staging = [&](int i) __attribute__((always_inline)) {
-      unsigned char* kdst = kbase + (P ^ 1) * KTILE;
-      unsigned char* vdst = vbase + P * VTILE;
-      if (i == 12) store_k(kdst);
-      if (i == 13) { store_v_pair(vdst, 0); store_v_pair(vdst, 1); }
-      if (i == 14) { store_v_pair(vdst, 2); store_v_pair(vdst, 3); }
-      // the four loads go out together, last: schedules that split them
-      // raised the L2 misses of the workgroups sharing a KV stream, up to
-      // eight times the HBM traffic in one measured case
-      if (i == 15) { load_k(t2); load_v(t1); }
+    auto stage = [&](int j) __attribute__((always_inline)) {
+      stage_block(j, t1, P ? kbuf0 : kbuf1, t0, P ? vbuf1 : vbuf0);
     };
+    auto stage_first4 = [&](int i) __attribute__((always_inline)) {
+      if (i < 4) stage(i);
+    };
+    auto nothing = [&](int) __attribute__((always_inline)) {};
     if (grp == 0) {
-      matrix_slot(kbc, vbc, staging);
+      matrix_slot(kbc, vbc, stage_first4);
     } else {
-      if (tm1.valid()) softmax_tile(tm1);
+      // also on tile -1 (iteration 0), where S^T = -inf makes it a no-op
+      // that leaves P^T = 0: the staging blocks are issued from inside it
+      softmax_tile(tm1, stage);
     }
-    __syncthreads();
+    slot_barrier();
     if (grp == 0) {
-      if (t0.valid()) softmax_tile(t0);
+      if (t0.valid()) softmax_tile(t0, nothing);
     } else {
-      matrix_slot(kbc, vbc, staging);
+      matrix_slot(kbc, vbc, nothing);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's staging has landed
+    slot_barrier();
     ti[(Q + 3) & 3] = next_info();  // tile n + 3 takes the place of tile n - 1
   };
   for (;;) {
