@@ -215,6 +215,9 @@ struct RunCursor {
   }
 };
 
+// EXACT: track the exact running maximum (chunk mode hands back the state
+// relative to it); ring mode needs only the reference.
+template <bool EXACT>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // four distinct arrays, so that the compiler can tell the buffer being
   // filled from the one being read and inserts no wait between them
@@ -370,35 +373,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
   };
 
-  // Vector work on a computed S^T: mask, maximum, reference update (rare O^T
-  // rescale), exponentials into P^T and the row sum.
-  // side(j), j = 0..3, is called at four points spread over the slot
-  auto softmax_tile = [&](const TileInfo& t, auto side) __attribute__((always_inline)) {
-    side(0);
-    if (t.need_mask()) apply_mask(t);
-    // two chains of three-input maxima over the lane's 32 scores
-    float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      mx0 = fmaxf(fmaxf(mx0, s[0][r]), s[0][r + 1]);
-      mx1 = fmaxf(fmaxf(mx1, s[1][r]), s[1][r + 1]);
-    }
-    const float mx = max_pair32(fmaxf(mx0, mx1)) * c2;
-    m_max = fmaxf(m_max, mx);
-    const bool grow = mx > m_ref + RESCALE_SLACK;  // also true when m_ref is -inf
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_ref;
-      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] *= alpha;
-    }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    side(1);
-    // The row sum adds the fp32 exponentials (four chains).  It is not taken
-    // with v_dot2 over the bf16 pairs: dot instructions wait for the matrix
-    // core, which the other wave of the SIMD keeps busy during this slot.
+  // Exponentials of a computed S^T against the reference m_use into P^T, and
+  // this lane's part of the tile's row sum (fp32 adds in four chains; not
+  // v_dot2 over the bf16 pairs: dot instructions wait for the matrix core,
+  // which the other wave of the SIMD keeps busy during this slot).
+  auto exponentials = [&](float m_use, auto side) __attribute__((always_inline)) -> float {
     float rs[4];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
@@ -414,7 +393,66 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
           r = e == 0 ? p0 + p1 : (r + p0) + p1;
           if (b2 == 0 && mm == 1 && e == 6) side(2);
         }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+  // Tile maximum (two chains of three-input maxima over the lane's 32 scores,
+  // then the other half-wave), in log2 units.
+  auto tile_max = [&]() __attribute__((always_inline)) -> float {
+    float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      mx0 = fmaxf(fmaxf(mx0, s[0][r]), s[0][r + 1]);
+      mx1 = fmaxf(fmaxf(mx1, s[1][r]), s[1][r + 1]);
+    }
+    return max_pair32(fmaxf(mx0, mx1)) * c2;
+  };
+  // Move the reference of the lanes where `grow` holds to mx (rescaling O^T
+  // and l); a no-op unless some lane grows.
+  auto move_reference = [&](bool grow, float mx) __attribute__((always_inline)) {
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_ref;
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] *= alpha;
+    }
+  };
+
+  // Vector work on a computed S^T: mask, reference update (rare O^T rescale),
+  // exponentials into P^T and the row sum.  side(j), j = 0..3, is called at
+  // four points spread over the work.
+  //   EXACT: the tile maximum first, as the pages' update does, tracking the
+  //     exact running maximum beside the reference (the state handed back by
+  //     the chunk entry point is relative to it); the reference moves when
+  //     the maximum exceeds it by more than RESCALE_SLACK.
+  //   otherwise: the exponentials first, against the current reference.  A
+  //     lane whose 32 values sum to at most 2^8 has every P^T value at most
+  //     2^8, the same bound the lazy reference keeps; if any lane's sum is
+  //     larger (or not finite, or the reference is still -inf) the tile maximum
+  //     is taken, the reference moves to it wherever it grew, and the
+  //     exponentials are recomputed.  The result is the same update with the
+  //     maximum skipped on nearly every tile.
+  auto softmax_tile = [&](const TileInfo& t, auto side) __attribute__((always_inline)) {
+    side(0);
+    if (t.need_mask()) apply_mask(t);
+    auto nothing = [](int) {};
+    if constexpr (EXACT) {
+      const float mx = tile_max();
+      m_max = fmaxf(m_max, mx);
+      move_reference(mx > m_ref + RESCALE_SLACK, mx);  // also true when m_ref is -inf
+      side(1);
+      l_run += exponentials(m_ref == -INFINITY ? 0.f : m_ref, side);
+    } else {
+      side(1);
+      float part = exponentials(m_ref, side);
+      if (__any(!(part <= 256.f) || m_ref == -INFINITY)) {
+        const float mx = tile_max();
+        move_reference(mx > m_ref, mx);
+        part = exponentials(m_ref == -INFINITY ? 0.f : m_ref, nothing);
+      }
+      l_run += part;
+    }
     side(3);
   };
 
@@ -522,7 +560,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   //   slot 2: A vector (softmax(n))  |  B matrix (QK(n), PV(n-1))
   // Staging of K(n+1) into K buffer (n+1) % 2 and of V(n) into V buffer n % 2
   // is issued in slot 1 by both groups, one 1 KiB block per wave at a time
-  // (group A between its first MFMA pairs, group B spread over its softmax),
+  // (group A between its last MFMA pairs, group B spread over its softmax),
   // and waited for at the end of slot 2; neither buffer is read in iteration n.
   auto iteration = [&](auto qc) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;   // n % 4
@@ -535,12 +573,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     auto stage = [&](int j) __attribute__((always_inline)) {
       stage_block(j, t1, P ? kbuf0 : kbuf1, t0, P ? vbuf1 : vbuf0);
     };
-    auto stage_first4 = [&](int i) __attribute__((always_inline)) {
-      if (i < 4) stage(i);
+    auto stage_last4 = [&](int i) __attribute__((always_inline)) {
+      if (i >= 12) stage(i - 12);
     };
     auto nothing = [&](int) __attribute__((always_inline)) {};
     if (grp == 0) {
-      matrix_slot(kbc, vbc, stage_first4);
+      matrix_slot(kbc, vbc, stage_last4);
     } else {
       // also on tile -1 (iteration 0), where S^T = -inf makes it a no-op
       // that leaves P^T = 0: the staging blocks are issued from inside it
@@ -620,7 +658,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.n_work <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(a.n_work), dim3(NTHREADS), 0, stream, a);
+  if (a.mode == MODE_CHUNK)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3(a.n_work), dim3(NTHREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(a.n_work), dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 
