@@ -149,6 +149,41 @@ def test_sharp_scores_running_max():
     assert max_abs(lse, ref_lse) <= TOL["bf16"] * 10  # lse ~ 40: relative 5e-3
 
 
+@pytest.mark.parametrize("profile", ["ramp_fast", "ramp_slow", "falling", "jumps"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_reference_updates(profile, causal):
+    """Scores whose maximum keeps growing along the keys (in log2 units per key:
+    0.1, 0.02, falling, and jumps of 12 every third tile of 64 keys) drive every
+    reference update of the online softmax: exponentials above 1 kept while
+    their sums stay small, a moved reference when they do not, and the exact
+    maximum taken when the growth is abrupt."""
+    print(f"case growing {profile} causal={causal}", flush=True)
+    w = synthetic.Workload("t", 1, 4, 2, 2048, 4, 128, "bf16", causal, "contiguous", seed=17)
+    q, k, v = synthetic.draw(w, device=DEV)
+    S, d = w.seq, w.d
+    pos = torch.arange(S, device=DEV, dtype=torch.float32)
+    if profile == "ramp_fast":
+        t = 0.1 * pos
+    elif profile == "ramp_slow":
+        t = 0.02 * pos
+    elif profile == "falling":
+        t = 60.0 - 0.05 * pos
+    else:
+        t = 12.0 * torch.div(pos, 192, rounding_mode="floor") + 0.5 * torch.sin(pos)
+    # q = 0.5 + noise, k = (t / (0.5 c d)) + noise: c q.k is about t (log2 units)
+    c = (1.0 / math.sqrt(d)) / math.log(2.0)
+    q = (0.5 + 0.05 * q.float()).to(torch.bfloat16)
+    k = ((t / (0.5 * c * d))[None, None, :, None] + 0.05 * k.float()).to(torch.bfloat16)
+    kp = api.to_chunked(k, w.layout, w.n_chunks)
+    vp = api.to_chunked(v, w.layout, w.n_chunks)
+    qp = api.to_chunked(q, w.layout, w.n_chunks)
+    out, lse = _ring(w, qp, kp, vp, out_dtype=torch.float32)
+    ref, ref_lse = oracle_all_rows(w, qp, k, v, causal)
+    assert max_abs(out, ref) <= TOL["bf16"]
+    # lse reaches about 200: relative 1e-4
+    assert max_abs(lse, ref_lse) <= 2e-4 * float(np.abs(np.asarray(ref_lse)).max()) + TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------
 # chunk update, finalize, merge
 # ---------------------------------------------------------------------------
