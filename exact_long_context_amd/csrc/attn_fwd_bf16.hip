@@ -456,42 +456,51 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     side(3);
   };
 
+  // MFMA operand reads from the K buffer KB / V buffer VB of a slot, step i
+  // (i = 0..15: QK half b2 = i % 2 at 16-key step i / 2, PV 16-key step
+  // i / 4 at dv block i % 4)
+  auto kread = [&](auto kbc, int i) __attribute__((always_inline)) {
+    const unsigned char* kb = decltype(kbc)::value ? kbuf1 : kbuf0;
+    return *(const bf16x8*)(kb + k_lane + (i & 1) * 8192 + (i >> 1) * 512);
+  };
+  auto vread = [&](auto vbc, int i) __attribute__((always_inline)) {
+    const unsigned char* vb = decltype(vbc)::value ? vbuf1 : vbuf0;
+    const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
+    const unsigned char* p = vb + v_lane[dvb] + (32 * pb2 + 16 * pmm) * ROWB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
+    const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  };
+  constexpr int AHEAD = 2;  // operand reads in flight per chain
+  bf16x8 kq[AHEAD], vq[AHEAD];
+  auto first_reads = [&](auto kbc, auto vbc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) {
+      kq[i] = kread(kbc, i);
+      vq[i] = vread(vbc, i);
+    }
+  };
+
   // Matrix slot: S^T of the tile in K buffer KB and O^T += V^T P^T with the
   // tile in V buffer VB; the two MFMA chains alternate so that each operand
   // read has time to land.  At the ends of the stream one half works on stale
   // or zero data: a QK with no tile behind it is never used, and the first PV
-  // multiplies P^T = 0 with a zeroed V buffer.
-  auto matrix_slot = [&](auto kbc, auto vbc, auto side) __attribute__((always_inline)) {
-    constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
-    const unsigned char* kb = KB ? kbuf1 : kbuf0;
-    const unsigned char* vb = VB ? vbuf1 : vbuf0;
-    auto kread = [&](int i) __attribute__((always_inline)) {
-      return *(const bf16x8*)(kb + k_lane + (i & 1) * 8192 + (i >> 1) * 512);
-    };
-    auto vread = [&](int i) __attribute__((always_inline)) {
-      const int pb2 = i >> 3, pmm = (i >> 2) & 1, dvb = i & 3;
-      const unsigned char* p = vb + v_lane[dvb] + (32 * pb2 + 16 * pmm) * ROWB;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
-      const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      return __builtin_bit_cast(bf16x8, w);
-    };
-    constexpr int AHEAD = 2;  // operand reads in flight per chain
-    bf16x8 kq[AHEAD], vq[AHEAD];
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) {
-      kq[i] = kread(i);
-      vq[i] = vread(i);
+  // multiplies P^T = 0 with a zeroed V buffer.  With `pre` the first reads
+  // were issued before the slot began.
+  auto matrix_slot = [&](auto kbc, auto vbc, auto side, auto pre) __attribute__((always_inline)) {
+    if constexpr (!decltype(pre)::value) {
+      first_reads(kbc, vbc);
+      __builtin_amdgcn_sched_barrier(0);  // the first reads go out before anything else
     }
-    __builtin_amdgcn_sched_barrier(0);  // the first reads go out before anything else
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bf16x8 kf = kq[i % AHEAD], vf = vq[i % AHEAD];
       if (i + AHEAD < 16) {
-        kq[i % AHEAD] = kread(i + AHEAD);
-        vq[i % AHEAD] = vread(i + AHEAD);
+        kq[i % AHEAD] = kread(kbc, i + AHEAD);
+        vq[i % AHEAD] = vread(vbc, i + AHEAD);
       }
       // keep the reads issued ahead of the two MFMAs that follow
       __builtin_amdgcn_sched_barrier(0);
@@ -546,10 +555,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // Barrier between slots.  Not __syncthreads(): its release fence would wait
   // for the staging loads in flight (they write LDS); the staging is waited
   // for explicitly before the second barrier of an iteration instead.  LDS
-  // reads have all been consumed by the end of a slot; the wait on them is
-  // kept for form's sake.
+  // reads may stay in flight across it (group B's first operands): no buffer
+  // read in an iteration is written before the next iteration.
   auto slot_barrier = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -577,18 +585,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       if (i >= 12) stage(i - 12);
     };
     auto nothing = [&](int) __attribute__((always_inline)) {};
+    const std::false_type read_first{};
+    const std::true_type prefetched{};
     if (grp == 0) {
-      matrix_slot(kbc, vbc, stage_last4);
+      matrix_slot(kbc, vbc, stage_last4, read_first);
     } else {
       // also on tile -1 (iteration 0), where S^T = -inf makes it a no-op
       // that leaves P^T = 0: the staging blocks are issued from inside it
       softmax_tile(tm1, stage);
+      // the first operands of this group's matrix slot: K(n) and V(n-1) are
+      // complete since the previous iteration
+      first_reads(kbc, vbc);
     }
     slot_barrier();
     if (grp == 0) {
       if (t0.valid()) softmax_tile(t0, nothing);
     } else {
-      matrix_slot(kbc, vbc, nothing);
+      matrix_slot(kbc, vbc, nothing, prefetched);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's staging has landed
     slot_barrier();
