@@ -15,9 +15,12 @@ Contents:
 * :mod:`oracle.attention` -- the plain definition of exact softmax attention,
   an independent chunked (m, l, o) loop in ring order, the single-chunk state
   update, finalize, and the log-sum-exp merge of two partials.
+* :mod:`oracle.backward` -- the gradients dq, dk, dv of exact attention by
+  the steps of the pages' backward listing, and the same steps taken in ring
+  order with P recomputed from the forward's log-sum-exp.
 
 Every function states the passage of the source pages it follows.  Pins
 (checks against things other than the oracle itself) live in
 ``tests/test_oracle_*.py``.  Nothing here is parity-unpinned.
 """
-from . import attention, layout  # noqa: F401
+from . import attention, backward, layout  # noqa: F401

@@ -100,3 +100,70 @@ def test_mutation_is_caught(fname, old, new):
     mut = _load(fname, old, new)
     failed = _pins(mut, LY) if fname == "attention.py" else _pins(A, mut)
     assert failed >= 1, f"no pin caught the mutation {old!r} -> {new!r}"
+
+
+# ---------------------------------------------------------------------------
+# backward.py
+# ---------------------------------------------------------------------------
+
+import tests.test_oracle_backward as TB  # noqa: E402
+
+
+def _load_backward(old, new):
+    src = open(os.path.join(ORACLE, "backward.py")).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new).replace("from .attention import", "from oracle.attention import")
+    mod = types.ModuleType("oracle_mutant_backward")
+    exec(compile(src, "<mutant backward.py>", "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_backward(BW):
+    saved = TB.BW
+    TB.BW = BW
+    calls = [
+        lambda: TB.test_gradient_matches_finite_differences(True, 4, 2),
+        lambda: TB.test_gradient_matches_finite_differences(False, 1, 1),
+        lambda: TB.test_key_shift_invariance_and_value_sum(True),
+        lambda: TB.test_single_key_and_uniform_rows(),
+        lambda: TB.test_ring_order_equals_definition("zigzag", True, [2]),
+        lambda: TB.test_ring_order_equals_definition("striped", False, [0, 1, 2, 3]),
+    ]
+    failed = 0
+    try:
+        for c in calls:
+            try:
+                c()
+            except Exception:
+                failed += 1
+    finally:
+        TB.BW = saved
+    return failed
+
+
+BACKWARD_MUTATIONS = [
+    # a dropped term, a wrong sign, transposed operands, a missing scale, the
+    # wrong head sum, a skipped ring step, a wrong lse use
+    ("dS = P * (dP - D[:, None]) * scale", "dS = P * dP * scale"),
+    ("dS = P * (dP - D[:, None]) * scale", "dS = P * (D[:, None] - dP) * scale"),
+    ("dvv[b, g] += P.T @ dout[b, h]", "dvv[b, g] += P.T @ q[b, h]"),
+    ("dq[b, h] = dS @ K", "dq[b, h] = dS @ V"),
+    ("dk[b, g] += dS.T @ q[b, h]", "dk[b, g] = dS.T @ q[b, h]"),
+    ("dP = dout[b, h] @ V.T", "dP = dout[b, h] @ K.T"),
+    ("D = (dout[b, h] * out).sum(axis=1)", "D = (dout[b, h] * out).sum(axis=0).mean() + 0 * out[:, 0]"),
+    ("dS = P * (dP - D[b, h][:, None]) * sc", "dS = P * (dP - D[b, h][:, None])"),
+    ("for t in range(N):\n            j = (i - t) % N\n            kpos", "for t in range(N - 1):\n            j = (i - t) % N\n            kpos"),
+    ("np.exp(s - np.where(fin, lse, 0.0)[:, None])", "np.exp(s + np.where(fin, lse, 0.0)[:, None])"),
+    ("dk[j][b, g] += dS.T @ qi[b, h]", "dk[j][b, g] += dS.T @ doi[b, h]"),
+]
+
+
+def test_unmutated_backward_passes_all_pins():
+    import oracle.backward as BW
+    assert _pins_backward(BW) == 0
+
+
+@pytest.mark.parametrize("old,new", BACKWARD_MUTATIONS, ids=[f"backward:{i}" for i in range(len(BACKWARD_MUTATIONS))])
+def test_backward_mutation_is_caught(old, new):
+    failed = _pins_backward(_load_backward(old, new))
+    assert failed >= 1, f"no pin caught the mutation {old!r} -> {new!r}"
