@@ -41,6 +41,30 @@ def ring_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, seq: int,
     return out, lse
 
 
+def ring_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                  lse: torch.Tensor, *, seq: int, n_chunks: int, layout: str, causal: bool, q_chunk_first: int = 0,
+                  scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of ``ring_forward`` for the query chunks held in ``q``.
+
+    q, out, dout: [B, Hq, n_q * L, d] (physical order; dout bf16); k, v:
+    [B, Hkv, seq, d] chunk-major; lse: [B, Hq, n_q * L] fp32 as ring_forward
+    returns it.  Returns fp32 (dq like q, dk and dv like k and v); dk and dv
+    hold the share of the given query rows."""
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        assert t.stride() == ref.stride(), "gradients take the strides of their inputs: pass contiguous tensors"
+    assert dout.stride() == out.stride() and dout.dtype == q.dtype
+    desc = ra.ring_desc(q, k, v, seq=seq, n_chunks=n_chunks, layout=layout, causal=causal,
+                        q_chunk_first=q_chunk_first, out=out, lse=lse, scale=scale)
+    need = ra.ra_ring_bwd_workspace_bytes(desc)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ra.ra_ring_bwd(desc, q, k, v, out, dout, lse, dq, dk, dv, workspace, need, stream)
+    return dq, dk, dv
+
+
 class ChunkState:
     """Running (m, l, o) of a query block, fp32, contiguous."""
 

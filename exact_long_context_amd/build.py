@@ -22,10 +22,10 @@ PROBE_SRC = "mfma_probe.hip"
 PROBE_LIB = os.path.join(PKG, "libramfmaprobe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["ringattn_abi.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "elementwise.hip"]
+SOURCES = ["ringattn_abi.cpp", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_fwd_f32.hip", "elementwise.hip"]
 # the bf16 kernel never produces NaN (masked scores are -inf, masked keys meet
 # zero V); without this flag every v_max_f32 gets a quieting max(x, x) first
-EXTRA_FLAGS = {"attn_fwd_bf16.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_bwd_bf16.hip": ["-fno-honor-nans"]}
 
 ARCH = "gfx950"
 # packed fp32 VALU forms are disabled for every HIP object (see the design notes)

@@ -1,0 +1,540 @@
+// Backward of ring-ordered exact attention, bf16 inputs, d = 128, for gfx950.
+//
+// The steps are those of ring_attention_backward on the youngju.dev page
+// ("Ring Attention 논문 분석", backward listing): with D = rowsum(dO * O) and
+// P = exp(s - lse) recomputed from the forward's log-sum-exp,
+//   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D) scale,  dQ = dS K,  dK = dS^T Q.
+// Three launches:
+//   * bwd_prep: per query row, -lse / scale and -D into the workspace;
+//   * attn_bwd_dq: per query tile (the forward's work decomposition), the KV
+//     tiles in ring order; dQ stays on chip;
+//   * attn_bwd_dkdv: per tile of 256 keys of one KV segment, every visible
+//     query row of the requested query chunks, for every query head of the
+//     KV head; dK and dV stay on chip, so their sums over the query heads and
+//     the query chunks need no atomics.
+// Every product is a v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and
+// dS are rounded to bf16 as MFMA operands.
+//
+// Layouts in LDS (as in the forward kernel): "natural" tiles, where an
+// operand read takes 16 rows at one 16-byte chunk (k_pos: blocks of 16 rows,
+// the 16-byte chunks of the 16 rows side by side), and "transposing" tiles
+// for ds_read_b64_tr_b16 (v_pos: row-major, chunk c of row r at c ^ 4 (r % 4)).
+// Tiles are filled by buffer loads that write LDS directly; rows past the end
+// of their segment arrive as zeros.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "fwd_common.h"
+#include "kernels.h"
+#include "schedule.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int D = 128;
+constexpr int ROWB = 2 * D;          // bytes of one bf16 row
+constexpr int TILE32 = 32 * ROWB;    // 8 KiB: 32 rows
+constexpr int NTHREADS = 512;
+constexpr float EMPTY_ROW = -1.0e30f;  // -lse / scale of a row that sees no key
+
+__device__ __forceinline__ int k_pos(int row, int chunk) { return (row >> 4) * 4096 + chunk * 256 + (row & 15) * 16; }
+__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Per-lane byte offsets for the DMA of one 1 KiB block.
+// natural tile: block blk (0..7 for 32 rows) = rows 16 (blk / 4) .. + 15, chunks 4 (blk % 4) .. + 3
+__device__ __forceinline__ uint32_t nat_src(int blk, int lane, uint32_t rs) {
+  return (uint32_t)(16 * (blk >> 2) + (lane & 15)) * rs + (uint32_t)(4 * (blk & 3) + (lane >> 4)) * 16;
+}
+// transposing tile: block blk = rows 4 blk .. 4 blk + 3; the lane landing on stored chunk lane % 16 of
+// row r fetches chunk (lane % 16) ^ 4 (r % 4), with r % 4 = lane / 16
+__device__ __forceinline__ uint32_t tr_src(int blk, int lane, uint32_t rs) {
+  return (uint32_t)(4 * blk + (lane >> 4)) * rs + (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) << 4);
+}
+
+__device__ __forceinline__ void dma(const void* base, uint32_t nrec, unsigned char* dst, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, (int)soff, 0, 0);
+}
+
+// Two transposing reads: lane 16 G + j gets rows 4 t .. 4 t + 3 of column c0 + 16 (G % 2) + j for the
+// first and rows + 4 for the second (see v_lane below), i.e. an MFMA A operand with 8 consecutive rows
+// along k.
+__device__ __forceinline__ bf16x8 tr_read(const unsigned char* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
+  const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Per-lane offset of the transposing operand of dv/d block dvb inside a v_pos tile: A operand rows
+// (dv or d) 32 dvb + l32, k (keys or queries) 8 g + 0..7; add 16 st rows for the 16-step st.
+__device__ __forceinline__ int v_lane_of(int lane, int dvb) {
+  const int G = lane >> 4, j = lane & 15, q = j >> 2, g = lane >> 5;
+  return (8 * g + q) * ROWB + ((((dvb ^ q) << 2) + 2 * (G & 1) + ((j & 3) >> 1)) << 4) + (j & 1) * 8;
+}
+
+// ---------------------------------------------------------------------------
+// prep: -lse / scale and -D per query row
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const FwdArgs& f = a.f;
+  const int64_t rows_total = (int64_t)f.batch * f.hq * a.q_rows;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;  // 8 of the 128 elements
+  if (row >= rows_total) return;
+  const int32_t r = (int32_t)(row % a.q_rows);
+  const int64_t bh = row / a.q_rows;
+  const int32_t h = (int32_t)(bh % f.hq), b = (int32_t)(bh / f.hq);
+  const int64_t o = (int64_t)b * f.out_sb + (int64_t)h * f.out_sh + (int64_t)r * f.out_ss + 8 * sub;
+  const bf16x8 dov = *(const bf16x8*)((const __bf16*)a.dout + o);
+  float acc = 0.f;
+  if (f.out_bf16) {
+    const bf16x8 ov = *(const bf16x8*)((const __bf16*)f.out + o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)dov[e], (float)ov[e], acc);
+  } else {
+    const f32x4 o0 = *(const f32x4*)((const float*)f.out + o);
+    const f32x4 o1 = *(const f32x4*)((const float*)f.out + o + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf((float)dov[e], o0[e], fmaf((float)dov[e + 4], o1[e], acc)) ;
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (sub == 0) {
+    const float lse = a.lse_in[(int64_t)b * f.ml_sb + (int64_t)h * f.ml_sh + r];
+    a.w[row] = lse == -INFINITY ? EMPTY_ROW : -lse / a.scale;
+    a.w[rows_total + row] = -acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: per query tile, the KV tiles of 32 keys in ring order
+// ---------------------------------------------------------------------------
+
+constexpr int BNQ = 32;
+
+__global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+  const FwdArgs& f = a.f;
+  // per buffer: K natural (S^T = K Q^T), K transposing (dQ^T += K^T dS^T), V natural (dP^T = V dO^T)
+  __shared__ __attribute__((aligned(1024))) unsigned char kn0[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char kn1[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char kt0[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char kt1[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char vn0[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char vn1[TILE32];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const WorkItem it = decode_work(f, blockIdx.x);
+  const QGeom qg = query_geom(f, it);
+  const int HP = f.heads_per_wg;
+  const int G = f.hq / f.hkv;
+  const int h = it.kvh * G + it.hg * HP + (wave % HP);
+  const int wg_p0 = it.tile * f.rows_per_wg;
+  const int p0 = __builtin_amdgcn_readfirstlane(wg_p0 + (wave / HP) * 32);
+  const int wg_p_hi = min(wg_p0 + f.rows_per_wg, qg.len) - 1;
+  const int my_p = p0 + l32;
+  const bool row_ok = my_p < qg.len;
+  const int64_t qrow = qg.row_base + my_p;
+
+  // Q and dO of this lane's query row as MFMA B operands
+  bf16x8 qf[8], dof[8];
+  {
+    const __bf16* qs = (const __bf16*)f.q + (int64_t)it.b * f.q_sb + (int64_t)h * f.q_sh + qrow * f.q_ss + 8 * g;
+    const __bf16* ds = (const __bf16*)a.dout + (int64_t)it.b * f.out_sb + (int64_t)h * f.out_sh + qrow * f.out_ss + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = row_ok ? *(const bf16x8*)(qs + 16 * ks) : bf16x8{};
+      dof[ks] = row_ok ? *(const bf16x8*)(ds + 16 * ks) : bf16x8{};
+    }
+  }
+  const float c2 = f.scale_log2;
+  const int64_t wrow = ((int64_t)it.b * f.hq + h) * a.q_rows + qrow;
+  const int64_t rows_total = (int64_t)f.batch * f.hq * a.q_rows;
+  const float w1c = row_ok ? a.w[wrow] * c2 : 0.f;            // -lse log2(e)
+  const float negD = row_ok ? a.w[rows_total + wrow] : 0.f;   // -D
+
+  const unsigned char* Kg = (const unsigned char*)f.k + ((int64_t)it.b * f.k_sb + (int64_t)it.kvh * f.k_sh) * 2;
+  const unsigned char* Vg = (const unsigned char*)f.v + ((int64_t)it.b * f.v_sb + (int64_t)it.kvh * f.v_sh) * 2;
+  const uint32_t kss = (uint32_t)(f.k_ss * 2), vss = (uint32_t)(f.v_ss * 2);
+  // DMA: wave w moves block w of each of the three tiles
+  const uint32_t kn_src = nat_src(wave, lane, kss), kt_src = tr_src(wave, lane, kss), vn_src = nat_src(wave, lane, vss);
+  const int blk_dst = __builtin_amdgcn_readfirstlane(wave * 1024);
+
+  const int k_lane = k_pos(kperm(l32), g);  // natural operand, 16-d step ks: + 512 ks
+  int v_lane[4];
+#pragma unroll
+  for (int dvb = 0; dvb < 4; ++dvb) v_lane[dvb] = v_lane_of(lane, dvb);
+
+  f32x16 acc[4];  // dQ^T[d = 32 dvb + 8 (r / 4) + 4 g + r % 4][query my_p]
+#pragma unroll
+  for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] = f32x16{};
+
+  TileCursor<BNQ> cur = make_cursor<BNQ>(f, qg, wg_p_hi < wg_p0 ? -1 : wg_p_hi);
+  if (wg_p_hi < wg_p0) cur.done = true;
+  auto stage = [&](const TileCursor<BNQ>& c, auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    const uint32_t nk = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * kss + ROWB;
+    const uint32_t nv = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * vss + ROWB;
+    const uint32_t sk = (uint32_t)(c.kv_row + c.k0) * kss, sv = (uint32_t)(c.kv_row + c.k0) * vss;
+    dma(Kg, nk, (B ? kn1 : kn0) + blk_dst, kn_src, sk);
+    dma(Kg, nk, (B ? kt1 : kt0) + blk_dst, kt_src, sk);
+    dma(Vg, nv, (B ? vn1 : vn0) + blk_dst, vn_src, sv);
+  };
+
+  auto compute = [&](const TileCursor<BNQ>& c, auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    const unsigned char* kn = B ? kn1 : kn0;
+    const unsigned char* kt = B ? kt1 : kt0;
+    const unsigned char* vn = B ? vn1 : vn0;
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma(*(const bf16x8*)(kn + k_lane + 512 * ks), qf[ks], s);
+      dp = mfma(*(const bf16x8*)(vn + k_lane + 512 * ks), dof[ks], dp);
+    }
+    // register r holds tile key 16 (r / 8) + 8 g + r % 8; hide keys past the segment end or the diagonal
+    const bool need_mask = (c.k0 + BNQ > c.kv_len) || (c.causal && c.k0 + BNQ - 1 > c.delta + p0);
+    if (need_mask) {
+      int lim = c.kv_len - 1 - c.k0;
+      if (c.causal) {
+        const int lc = my_p + c.delta - c.k0;
+        lim = lc < lim ? lc : lim;
+      }
+      lim = (lim < -1 ? -1 : (lim > 1000 ? 1000 : lim)) - 8 * g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 16 * (r >> 3) + (r & 7);
+        s[r] = kk > lim ? -INFINITY : s[r];
+      }
+    }
+    bf16x8 dsf[2];  // dS^T as B operands: dsf[st] holds keys 16 st + 8 g + 0..7
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, w1c));
+      dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] + negD));
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int dvb = 0; dvb < 4; ++dvb)
+        acc[dvb] = mfma(tr_read(kt + v_lane[dvb] + 16 * st * ROWB), dsf[st], acc[dvb]);
+  };
+
+  // double buffer: tile n in buffer n % 2; tile n + 1 is staged while tile n is computed
+  if (!cur.done) stage(cur, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  auto step = [&](auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    TileCursor<BNQ> nxt = cur;
+    nxt.advance();
+    if (!nxt.done) stage(nxt, std::integral_constant<int, B ^ 1>{});
+    compute(cur, bc);
+    cur = nxt;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  while (!cur.done) {
+    step(std::integral_constant<int, 0>{});
+    if (cur.done) break;
+    step(std::integral_constant<int, 1>{});
+  }
+
+  if (!row_ok) return;
+  float* dqrow = a.dq + (int64_t)it.b * f.q_sb + (int64_t)h * f.q_sh + qrow * f.q_ss;
+  const float sc = a.scale;
+#pragma unroll
+  for (int dvb = 0; dvb < 4; ++dvb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = acc[dvb][r4 * 4 + e] * sc;
+      *(f32x4*)(dqrow + dvb * 32 + r4 * 8 + 4 * g) = v4;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: per 256 keys of one KV segment, the visible query rows in steps of 32
+// ---------------------------------------------------------------------------
+
+constexpr int KV_TILE = 256;  // keys per workgroup: 8 waves x 32
+constexpr int BQ = 32;        // query rows per step
+
+// Uniform walk over the steps of a workgroup: requested query chunk, its query
+// segments, the query heads of the KV head, query row tiles of BQ.
+struct StepCursor {
+  int32_t ci, qs, hh, p0;   // query chunk index (relative), segment, head in group, first row
+  int32_t qlen, p_start, delta, causal, kind_ok;
+  int64_t q_row0;           // buffer row of the query segment's row 0
+  bool done;
+};
+
+__global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  const FwdArgs& f = a.f;
+  // per buffer: Q natural (S = Q K^T), Q transposing (dK^T += Q^T dS), dO natural (dP = dO V^T),
+  // dO transposing (dV^T += dO^T P), and the two per-row terms
+  __shared__ __attribute__((aligned(1024))) unsigned char qn0[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char qn1[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char qt0[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char qt1[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char on0[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char on1[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char ot0[TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char ot1[TILE32];
+  __shared__ __attribute__((aligned(256))) float w0[2 * BQ];
+  __shared__ __attribute__((aligned(256))) float w1[2 * BQ];
+  // V of the workgroup's 256 keys, natural layout, for the whole launch
+  __shared__ __attribute__((aligned(1024))) unsigned char vs[KV_TILE * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  // work item: (b, kvh, KV chunk j, segment sb, key tile kt)
+  const int32_t nseg = num_segments(f.layout);
+  const int32_t L = f.lq;
+  int32_t w = blockIdx.x;
+  const int32_t kt = w % a.kv_tiles_per_seg; w /= a.kv_tiles_per_seg;
+  const int32_t sb = w % nseg; w /= nseg;
+  const int32_t j = w % f.n_chunks; w /= f.n_chunks;
+  const int32_t kvh = w % f.hkv;
+  const int32_t b = w / f.hkv;
+  const Segment kseg = segment_l(f.layout, L, f.n_chunks, j, sb);
+  const int64_t k_row0 = (int64_t)j * L + kseg.row0;  // buffer row of the segment's row 0
+  const int32_t kv_len = kseg.len;
+  const int32_t k_lo = kt * KV_TILE;                    // first key of the workgroup (segment rows)
+  const int32_t kw0 = k_lo + 32 * wave;                 // first key of this wave
+  const int32_t my_k = kw0 + l32;
+  const bool key_ok = my_k < kv_len;
+  const bool wave_live = kw0 < kv_len;
+  const int G = f.hq / f.hkv;
+
+  const uint32_t vss = (uint32_t)(f.v_ss * 2);
+  const uint32_t qss = (uint32_t)(f.q_ss * 2), oss = (uint32_t)(f.out_ss * 2);
+  const unsigned char* Kg = (const unsigned char*)f.k + ((int64_t)b * f.k_sb + (int64_t)kvh * f.k_sh) * 2;
+  const unsigned char* Vg = (const unsigned char*)f.v + ((int64_t)b * f.v_sb + (int64_t)kvh * f.v_sh) * 2;
+
+  // K of this lane's key as MFMA B operands (S = Q K^T: B = K^T, lane = key)
+  bf16x8 kf[8];
+  {
+    const __bf16* ks = (const __bf16*)(Kg) + (k_row0 + my_k) * f.k_ss + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = key_ok ? *(const bf16x8*)(ks + 16 * s) : bf16x8{};
+  }
+  // V of the workgroup's keys into LDS (8 blocks per wave; rows past the segment end read zero)
+  {
+    const uint32_t nv = (uint32_t)(k_row0 + kv_len - 1) * vss + ROWB;
+    const uint32_t sv = (uint32_t)(k_row0 + k_lo) * vss;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int blk = 8 * wave + i;  // rows 16 (blk / 4) .., chunks 4 (blk % 4) ..
+      dma(Vg, nv, vs + __builtin_amdgcn_readfirstlane(blk * 1024), nat_src(blk, lane, vss), sv);
+    }
+  }
+
+  const float c2 = f.scale_log2;
+  const int64_t rows_total = (int64_t)f.batch * f.hq * a.q_rows;
+  const uint32_t w_bytes = (uint32_t)(2 * rows_total * 4);
+  const int q_lane = k_pos(kperm(l32), g);        // natural operand (query rows permuted): + 512 ks
+  const int vb_lane = k_pos(32 * wave + l32, g);  // V as B operand (lane = key): + 512 s
+  int t_lane[4];
+#pragma unroll
+  for (int dvb = 0; dvb < 4; ++dvb) t_lane[dvb] = v_lane_of(lane, dvb);
+  const uint32_t qn_src = nat_src(wave, lane, qss), qt_src = tr_src(wave, lane, qss);
+  const uint32_t on_src = nat_src(wave, lane, oss), ot_src = tr_src(wave, lane, oss);
+  const int blk_dst = __builtin_amdgcn_readfirstlane(wave * 1024);
+
+  f32x16 acck[4], accv[4];  // dK^T / dV^T[d = 32 dvb + 8 (r / 4) + 4 g + r % 4][key my_k]
+#pragma unroll
+  for (int dvb = 0; dvb < 4; ++dvb) acck[dvb] = accv[dvb] = f32x16{};
+
+  // ---- step walk
+  auto load_seg = [&](StepCursor& c) __attribute__((always_inline)) {
+    // set up query segment (ci, qs); kind_ok = 0 when no row of it sees a key of the workgroup
+    const int32_t qchunk = f.q_first + c.ci;
+    const Segment qseg = segment_l(f.layout, L, f.n_chunks, qchunk, c.qs);
+    c.qlen = qseg.len;
+    c.q_row0 = (int64_t)c.ci * L + qseg.row0;
+    int64_t dl = f.causal ? pair_delta(qseg, kseg) : 0;
+    const int64_t lim = (int64_t)1 << 30;
+    c.delta = (int32_t)(dl > lim ? lim : (dl < -lim ? -lim : dl));
+    int64_t ps = 0;
+    if (f.causal) {
+      ps = (int64_t)k_lo - dl;  // key k_lo is visible from query row k_lo - delta on
+      ps = ps < 0 ? 0 : ps;
+    }
+    c.p_start = (int32_t)(ps > c.qlen ? c.qlen : ps);
+    c.kind_ok = (k_lo < kv_len) && (c.p_start < c.qlen);
+    c.p0 = c.p_start;
+    c.hh = 0;
+  };
+  auto skip_empty = [&](StepCursor& c) __attribute__((always_inline)) {
+    while (!c.done && !c.kind_ok) {
+      if (++c.qs >= nseg) { c.qs = 0; ++c.ci; }
+      if (c.ci >= f.q_count) { c.done = true; break; }
+      load_seg(c);
+    }
+  };
+  auto advance = [&](StepCursor& c) __attribute__((always_inline)) {
+    c.p0 += BQ;
+    if (c.p0 >= c.qlen) {
+      c.p0 = c.p_start;
+      if (++c.hh >= G) {
+        c.hh = 0;
+        c.kind_ok = 0;  // next segment
+        skip_empty(c);
+      }
+    }
+  };
+  StepCursor cur;
+  cur.ci = 0; cur.qs = 0; cur.done = false; cur.causal = f.causal;
+  load_seg(cur);
+  skip_empty(cur);
+
+  auto stage = [&](const StepCursor& c, auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    const int h = kvh * G + c.hh;
+    const unsigned char* Qg = (const unsigned char*)f.q + ((int64_t)b * f.q_sb + (int64_t)h * f.q_sh) * 2;
+    const unsigned char* Og = (const unsigned char*)a.dout + ((int64_t)b * f.out_sb + (int64_t)h * f.out_sh) * 2;
+    const int64_t end = c.q_row0 + c.qlen - 1;
+    const uint32_t nq = (uint32_t)end * qss + ROWB, no = (uint32_t)end * oss + ROWB;
+    const uint32_t sq = (uint32_t)(c.q_row0 + c.p0) * qss, so = (uint32_t)(c.q_row0 + c.p0) * oss;
+    dma(Qg, nq, (B ? qn1 : qn0) + blk_dst, qn_src, sq);
+    dma(Qg, nq, (B ? qt1 : qt0) + blk_dst, qt_src, sq);
+    dma(Og, no, (B ? on1 : on0) + blk_dst, on_src, so);
+    dma(Og, no, (B ? ot1 : ot0) + blk_dst, ot_src, so);
+    if (wave == 0 && lane < 16) {
+      // lanes 0..7: -lse / scale of the 32 rows; lanes 8..15: -D
+      const uint32_t row = (uint32_t)(((int64_t)b * f.hq + h) * a.q_rows + c.q_row0 + c.p0);
+      const uint32_t off = (row + 4 * (lane & 7)) * 4 + (lane >= 8 ? (uint32_t)(rows_total * 4) : 0u);
+      dma(a.w, w_bytes, (unsigned char*)(B ? w1 : w0), off, 0u);
+    }
+  };
+
+  auto compute = [&](const StepCursor& c, auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    const unsigned char* qn = B ? qn1 : qn0;
+    const unsigned char* qt = B ? qt1 : qt0;
+    const unsigned char* on = B ? on1 : on0;
+    const unsigned char* ot = B ? ot1 : ot0;
+    const float* wt = B ? w1 : w0;
+    // register r of lane (key l32, g) holds query row 16 (r / 8) + 8 g + r % 8 of the step
+    f32x16 s, dp;
+    {
+      const f32x4 a0 = *(const f32x4*)(wt + 8 * g), a1 = *(const f32x4*)(wt + 8 * g + 4);
+      const f32x4 a2 = *(const f32x4*)(wt + 16 + 8 * g), a3 = *(const f32x4*)(wt + 16 + 8 * g + 4);
+      const f32x4 b0 = *(const f32x4*)(wt + BQ + 8 * g), b1 = *(const f32x4*)(wt + BQ + 8 * g + 4);
+      const f32x4 b2 = *(const f32x4*)(wt + BQ + 16 + 8 * g), b3 = *(const f32x4*)(wt + BQ + 16 + 8 * g + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[e] = a0[e]; s[4 + e] = a1[e]; s[8 + e] = a2[e]; s[12 + e] = a3[e];
+        dp[e] = b0[e]; dp[4 + e] = b1[e]; dp[8 + e] = b2[e]; dp[12 + e] = b3[e];
+      }
+    }
+    // S + (-lse / scale) and dP + (-D)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma(*(const bf16x8*)(qn + q_lane + 512 * ks), kf[ks], s);
+      dp = mfma(*(const bf16x8*)(on + q_lane + 512 * ks), *(const bf16x8*)(vs + vb_lane + 512 * ks), dp);
+    }
+    // hide rows past the segment end and pairs past the diagonal
+    const bool need_mask = (c.p0 + BQ > c.qlen) || (c.causal && kw0 + 31 - c.p0 > c.delta);
+    if (need_mask) {
+      const int hi = c.qlen - c.p0 - 8 * g;                       // rows >= hi are past the end
+      const int lo = c.causal ? my_k - c.p0 - c.delta - 8 * g : -1000000;  // rows < lo are before the key
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qo = 16 * (r >> 3) + (r & 7);
+        s[r] = (qo >= hi || qo < lo) ? -INFINITY : s[r];
+      }
+    }
+    bf16x8 pb[2], db[2];  // P and dS as B operands: [st] holds query rows 16 st + 8 g + 0..7
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[r] * c2);
+      pb[r >> 3][r & 7] = (__bf16)p;
+      db[r >> 3][r & 7] = (__bf16)(p * dp[r]);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int dvb = 0; dvb < 4; ++dvb) {
+        accv[dvb] = mfma(tr_read(ot + t_lane[dvb] + 16 * st * ROWB), pb[st], accv[dvb]);
+        acck[dvb] = mfma(tr_read(qt + t_lane[dvb] + 16 * st * ROWB), db[st], acck[dvb]);
+      }
+  };
+
+  if (!cur.done) stage(cur, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // V and the first step are in LDS
+  __syncthreads();
+  auto step = [&](auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    StepCursor nxt = cur;
+    advance(nxt);
+    if (!nxt.done) stage(nxt, std::integral_constant<int, B ^ 1>{});
+    if (wave_live) compute(cur, bc);
+    cur = nxt;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  while (!cur.done) {
+    step(std::integral_constant<int, 0>{});
+    if (cur.done) break;
+    step(std::integral_constant<int, 1>{});
+  }
+
+  if (!key_ok) return;
+  const int64_t krow = k_row0 + my_k;
+  float* dkrow = a.dk + (int64_t)b * f.k_sb + (int64_t)kvh * f.k_sh + krow * f.k_ss;
+  float* dvrow = a.dv + (int64_t)b * f.v_sb + (int64_t)kvh * f.v_sh + krow * f.v_ss;
+  const float sc = a.scale;
+#pragma unroll
+  for (int dvb = 0; dvb < 4; ++dvb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 k4, v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k4[e] = acck[dvb][r4 * 4 + e] * sc;
+        v4[e] = accv[dvb][r4 * 4 + e];
+      }
+      *(f32x4*)(dkrow + dvb * 32 + r4 * 8 + 4 * g) = k4;
+      *(f32x4*)(dvrow + dvb * 32 + r4 * 8 + 4 * g) = v4;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows_total = (int64_t)a.f.batch * a.f.hq * a.q_rows;
+  if (rows_total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows_total + 15) / 16)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream) {
+  if (a.f.n_work <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(a.f.n_work), dim3(NTHREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, hipStream_t stream) {
+  if (a.n_work_kv <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(a.n_work_kv), dim3(NTHREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ra

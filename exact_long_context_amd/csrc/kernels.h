@@ -56,6 +56,30 @@ struct FwdArgs {
 };
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+
+// Arguments of the backward kernels (bf16 inputs, d = 128, ring mode).  `f`
+// carries q, k, v, their strides, the ring geometry and the dQ work
+// decomposition (the forward's); out and dout share the out strides.
+struct BwdArgs {
+  FwdArgs f;
+  const void* dout;
+  const float* lse_in;  // natural log-sum-exp of the forward, strides f.ml_sb / f.ml_sh
+  float* dq;            // fp32, strides of q
+  float* dk;            // fp32, strides of k
+  float* dv;            // fp32, strides of v
+  float* w;             // workspace: two fp32 per (b, query head, row), see launch_bwd_prep
+  int32_t q_rows;       // query rows per (b, head): q_count * L
+  float scale;          // score scale
+  // dK/dV work decomposition: key tiles of 256 rows per KV segment
+  int32_t kv_tiles_per_seg;
+  int32_t n_work_kv;
+};
+
+// w[0 .. B*Hq*q_rows): -lse / scale (a large negative value for lse = -inf);
+// w[B*Hq*q_rows ..): -rowsum(dout * out)
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 struct RowsArgs {  // [B, H, rows] fp32 tensors with strides (b, h), row stride 1; o-like with (b, h, s)

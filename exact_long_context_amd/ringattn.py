@@ -78,6 +78,9 @@ _sigs = {
     "ra_merge": (ctypes.c_int, [_P(ra_attn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ra_ring_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
     "ra_ring_fwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ra_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
+    "ra_ring_bwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   ctypes.c_size_t, _vp]),
     "ra_layout_positions": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            _P(ctypes.c_int64)]),
     "ra_ring_schedule": (ctypes.c_int, [_P(ra_ring_desc), ctypes.c_int32, _P(ra_task), ctypes.c_int32,
@@ -220,6 +223,17 @@ def ra_ring_fwd(desc: ra_ring_desc, q, k, v, out, lse=None, workspace=None, work
                 stream=None):
     _check(_lib.ra_ring_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                             workspace_bytes, _stream(stream)), "ra_ring_fwd")
+
+
+def ra_ring_bwd_workspace_bytes(desc: ra_ring_desc) -> int:
+    return int(_lib.ra_ring_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def ra_ring_bwd(desc: ra_ring_desc, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes: int,
+                stream=None):
+    _check(_lib.ra_ring_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "ra_ring_bwd")
 
 
 def ra_layout_positions(layout, seq: int, n_chunks: int, chunk: int) -> np.ndarray:

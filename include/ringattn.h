@@ -1,6 +1,6 @@
 /*
- * libringattn -- exact ring-ordered attention forward for AMD Instinct MI355X
- * (gfx950).
+ * libringattn -- exact ring-ordered attention (forward and backward) for AMD
+ * Instinct MI355X (gfx950).
  *
  * The method (sources: the youngju.dev page "Ring Attention 논문 분석", the
  * Ultralytics glossary page "Ring Attention", the GPU MODE lecture 013 notes
@@ -195,6 +195,38 @@ size_t ra_ring_workspace_bytes(const ra_ring_desc* desc);
 ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v,
                       void* out, float* lse, void* workspace, size_t workspace_bytes,
                       ra_stream stream);
+
+/* Workspace bytes ra_ring_bwd needs for this descriptor: two fp32 values per
+ * (batch, query head, query row) of the requested query chunks. */
+size_t ra_ring_bwd_workspace_bytes(const ra_ring_desc* desc);
+
+/* Backward of ra_ring_fwd for the requested query chunks: the steps of
+ * ring_attention_backward on the youngju.dev page.  Per query row
+ * D = rowsum(dout * out); per visible (query, key) pair P = exp(s - lse) is
+ * recomputed from the forward's log-sum-exp, and
+ *   dv += P^T dout,  dP = dout v^T,  dS = P (dP - D) scale,
+ *   dq += dS k,      dk += dS^T q,
+ * visiting the KV chunks in ring order for dq and every requested query row
+ * for dk, dv.  With grouped heads dk and dv of a KV head sum the
+ * contributions of all its query heads.
+ * Inputs (device): q, k, v as for ra_ring_fwd; out (the forward's output,
+ * desc.attn.out_dtype, strides desc.attn.out); dout (bf16, strides
+ * desc.attn.out); lse (natural, fp32, strides desc.attn.ml) as ra_ring_fwd
+ * writes it.
+ * Outputs (device, fp32, overwritten): dq with the element strides of q;
+ * dk and dv with the element strides of k and v, for all n_chunks chunks:
+ * the share of the requested query rows (the full gradient when every query
+ * chunk is requested; on several devices these shares are what the pages'
+ * listing reduces to the owner of each KV chunk).  Keys no requested row
+ * sees get 0.
+ * workspace: device memory of ra_ring_bwd_workspace_bytes(desc) bytes, 16-byte
+ * aligned, used during the call only.
+ * Supported: in_dtype BF16 with d = 128 (RA_ERR_UNSUPPORTED otherwise); the
+ * limits of ra_ring_fwd apply, and one head's query and dout rows must also
+ * span less than 2 GiB.  Three kernels are enqueued on `stream`. */
+ra_status ra_ring_bwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                      size_t workspace_bytes, ra_stream stream);
 
 /* Host only.  pos[p] = global token position of row p of chunk `chunk`
  * (p = 0 .. seq/n_chunks - 1) under `layout`.  pos is host memory of
