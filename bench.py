@@ -87,6 +87,41 @@ def time_workload(w, steps, warmup, api, torch):
     return ms, wall
 
 
+def time_backward(w, steps, warmup, api, torch):
+    """ra_ring_bwd on the workload: the library's forward output and lse (not
+    timed) and a seeded upstream gradient as inputs, inputs and outputs
+    resident in HBM; HIP events on the launch stream around `steps` calls."""
+    import synthetic
+    from exact_long_context_amd import ringattn as ra
+    q, k, v = synthetic.draw(w, device="cuda")
+    kp = api.to_chunked(k, w.layout, w.n_chunks)
+    vp = api.to_chunked(v, w.layout, w.n_chunks)
+    qp = api.to_chunked(q, w.layout, w.n_chunks) if w.q_chunks is None else q
+    del q, k, v
+    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=w.causal,
+                                q_chunk_first=w.query_chunks[0])
+    dout = synthetic.normal_draw(qp.shape, w.seed + 101, dtype=torch.bfloat16, device="cuda")
+    dq = torch.empty(qp.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(kp.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(vp.shape, dtype=torch.float32, device="cuda")
+    desc = ra.ring_desc(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=w.causal,
+                        q_chunk_first=w.query_chunks[0], out=out, lse=lse)
+    nws = ra.ra_ring_bwd_workspace_bytes(desc)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ra.ra_ring_bwd(desc, qp, kp, vp, out, dout, lse, dq, dk, dv, ws, nws, stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ra.ra_ring_bwd(desc, qp, kp, vp, out, dout, lse, dq, dk, dv, ws, nws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def balance_report(w, api, torch):
     """Per-query-chunk work of a causal workload in its own layout and in the
     contiguous layout at the same shape: visible pairs from the schedule and the
@@ -225,6 +260,9 @@ def main():
     ap.add_argument("--workload", default="zigzag_1m_gqa")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time ra_ring_bwd on the workload (for profiling) and exit")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain 1 GiB device copies (counter calibration) and exit")
     ap.add_argument("--mfma-ceiling", action="store_true",
@@ -274,6 +312,10 @@ def main():
 
     w = synthetic.WORKLOADS[args.workload]
     flop = workload_flop(w, ra)
+    if args.backward_only:
+        bms = time_backward(w, args.steps, args.warmup, api, torch)
+        print(json.dumps({"backward_ms": round(bms, 3), "tflops": round(2.5 * flop / (bms * 1e-3) / 1e12, 2)}))
+        return
     log(f"workload {w.name}: {flop:.4e} FLOP per step (causal-adjusted)")
     ms, wall = time_workload(w, args.steps, args.warmup, api, torch)
     tflops = flop / (ms * 1e-3) / 1e12
@@ -294,6 +336,18 @@ def main():
                     log(f"    {lay}: visible pairs max/min {r['visible_pairs_max_over_min']}, "
                         f"time max/min {r['ms_max_over_min']}")
                 torch.cuda.empty_cache()
+
+    backward = None
+    if not args.no_backward:
+        torch.cuda.empty_cache()
+        bms = time_backward(w, max(2, args.steps // 3), 1, api, torch)
+        bflop = 2.5 * flop  # five products of 2 d per visible pair (S recomputed, dP, dV, dQ, dK)
+        btf = bflop / (bms * 1e-3) / 1e12
+        backward = {"entry_point": "ra_ring_bwd", "ms": round(bms, 3), "tflops": round(btf, 2),
+                    "flop_per_step": bflop, "frac_of_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+                    "flop_rule": "10 d per visible (query, key) pair and query head (2.5 x the forward)"}
+        log(f"  backward: {bms:.3f} ms  {btf:.1f} TFLOP/s ({btf / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 peak)")
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
@@ -325,6 +379,7 @@ def main():
                      "traffic": traffic_record()},
         "cpu_baseline": cpu,
         "other_workloads": others,
+        "backward": backward,
     }
     print(json.dumps(res))
 

@@ -68,3 +68,53 @@ def test_full_causal_sampled_rows(name, n):
         rs2 = torch.tensor([r for _, r in s2], device=out2.device)
         assert max_abs(out2[0, hs2, rs2].float().cpu().double().numpy(), ref2) <= TOL["bf16"]
         assert max_abs(lse2[0, hs2, rs2].cpu().double().numpy(), ref2_lse) <= TOL["bf16"]
+
+
+def test_full_backward_zigzag_1m_sampled():
+    """ra_ring_bwd at the 1M-token zig-zag GQA shape, in the configuration the
+    bench times (the library's forward output and lse as inputs): dq on a
+    seeded sample of query rows against the oracle (each row against all its
+    visible keys); dk and dv finite everywhere, with the sums over the keys of
+    each KV head that hold at any size (key gradients cancel; value gradients
+    add up to the upstream gradients within the bf16 rounding of the
+    weights)."""
+    from oracle import backward as OB
+    from .parity_utils import query_rows_positions
+    w = synthetic.WORKLOADS["zigzag_1m_gqa"]
+    print("case full backward zigzag_1m_gqa", flush=True)
+    qp, kp, vp, q, k, v = physical_inputs(w)
+    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=True)
+    do = synthetic.normal_draw(qp.shape, 77, dtype=torch.bfloat16, device="cuda")
+    dq, dk, dv = api.ring_backward(qp, kp, vp, out, do, lse, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout,
+                                   causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    G = w.hq // w.hkv
+    for g in range(w.hkv):
+        ksum = dk[0, g].double().sum(dim=0).abs()
+        assert (ksum <= 0.02 * dk[0, g].double().abs().sum(dim=0) + 1e-3).all()
+        rows = do[0, g * G:(g + 1) * G].double()
+        bound = rows.abs().sum(dim=(0, 1)) * 2.0 ** -9 + 1e-2
+        assert ((dv[0, g].double().sum(dim=0) - rows.sum(dim=(0, 1))).abs() <= bound).all()
+    del kp, vp
+    samples = sample_rows(w, 48, seed=1234)
+    qpos = query_rows_positions(w)
+    qc, doc = qp.cpu(), do.cpu()
+    by_kv = {}
+    for i, (h, r) in enumerate(samples):
+        by_kv.setdefault(h // G, []).append(i)
+    want = np.zeros((len(samples), w.d))
+    for g, idx in by_kv.items():
+        # the sampled rows of the group's heads as one block of rows against KV head g
+        kg, vg = k[:, g:g + 1].cpu(), v[:, g:g + 1].cpu()
+        hs_, rs_ = [samples[i][0] for i in idx], [samples[i][1] for i in idx]
+        qsel = torch.stack([qc[0, h, r] for h, r in zip(hs_, rs_)])[None, None]
+        dsel = torch.stack([doc[0, h, r] for h, r in zip(hs_, rs_)])[None, None]
+        dqr, _, _ = OB.attention_backward_reference(qsel, kg, vg, dsel, causal=True, q_pos=qpos[rs_],
+                                                    k_pos=np.arange(w.seq))
+        want[idx] = dqr[0, 0]
+    hs = torch.tensor([h for h, _ in samples], device=dq.device)
+    rs = torch.tensor([r for _, r in samples], device=dq.device)
+    err = max_abs(dq[0, hs, rs].cpu().double().numpy(), want)
+    print(f"  dq max-abs error on {len(samples)} rows {err:.2e} (magnitude {np.abs(want).max():.2e})", flush=True)
+    assert err <= TOL["bf16"]
