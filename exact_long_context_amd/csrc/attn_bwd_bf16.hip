@@ -276,10 +276,10 @@ constexpr int KV_TILE = 256;  // keys per workgroup: 8 waves x 32
 constexpr int BQ = 32;        // query rows per step
 
 // Uniform walk over the steps of a workgroup: requested query chunk, its query
-// segments, the query heads of the KV head, query row tiles of BQ.
+// segments, query row tiles of BQ, the query heads of the KV head.
 struct StepCursor {
   int32_t ci, qs, hh, p0;   // query chunk index (relative), segment, head in group, first row
-  int32_t qlen, p_start, delta, causal, kind_ok;
+  int32_t qlen, p_start, p_top, delta, causal, kind_ok;
   int64_t q_row0;           // buffer row of the query segment's row 0
   bool done;
 };
@@ -376,9 +376,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
       ps = (int64_t)k_lo - dl;  // key k_lo is visible from query row k_lo - delta on
       ps = ps < 0 ? 0 : ps;
     }
-    c.p_start = (int32_t)(ps > c.qlen ? c.qlen : ps);
-    c.kind_ok = (k_lo < kv_len) && (c.p_start < c.qlen);
-    c.p0 = c.p_start;
+    c.kind_ok = (k_lo < kv_len) && (ps < c.qlen);
+    // row tiles aligned to BQ, walked from the segment end down: the
+    // workgroups of one KV head then stream the same query rows at about the
+    // same time whatever their first visible row (rows below it are masked)
+    c.p_start = (int32_t)(ps < c.qlen ? ps : c.qlen) / BQ * BQ;
+    c.p_top = (c.qlen - 1) / BQ * BQ;
+    c.p0 = c.p_top;
     c.hh = 0;
   };
   auto skip_empty = [&](StepCursor& c) __attribute__((always_inline)) {
@@ -388,15 +392,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
       load_seg(c);
     }
   };
+  // inside a query segment: row tiles from the top down, the heads of the
+  // group inner, so that all workgroups walk the same rows in step
   auto advance = [&](StepCursor& c) __attribute__((always_inline)) {
-    c.p0 += BQ;
-    if (c.p0 >= c.qlen) {
-      c.p0 = c.p_start;
-      if (++c.hh >= G) {
-        c.hh = 0;
-        c.kind_ok = 0;  // next segment
-        skip_empty(c);
-      }
+    if (++c.hh < G) return;
+    c.hh = 0;
+    c.p0 -= BQ;
+    if (c.p0 < c.p_start) {
+      c.kind_ok = 0;  // next segment
+      skip_empty(c);
     }
   };
   StepCursor cur;
