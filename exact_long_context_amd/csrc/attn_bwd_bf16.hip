@@ -68,6 +68,21 @@ __device__ __forceinline__ void dma(const void* base, uint32_t nrec, unsigned ch
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, (int)soff, 0, 0);
 }
 
+// The same load written out, for kernels that manage vmcnt themselves: the compiler does not track
+// it, so it inserts no waits of its own before LDS reads it cannot tell apart from the load's target.
+// dst is a wave-uniform LDS byte address.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_untracked(const void* base, uint32_t nrec, uint32_t dst, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, 0x00020000);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Two transposing reads: lane 16 G + j gets rows 4 t .. 4 t + 3 of column c0 + 16 (G % 2) + j for the
 // first and rows + 4 for the second (see v_lane below), i.e. an MFMA A operand with 8 consecutive rows
 // along k.
@@ -286,20 +301,16 @@ struct StepCursor {
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
-  // per buffer: Q natural (S = Q K^T), Q transposing (dK^T += Q^T dS), dO natural (dP = dO V^T),
-  // dO transposing (dV^T += dO^T P), and the two per-row terms
-  __shared__ __attribute__((aligned(1024))) unsigned char qn0[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char qn1[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char qt0[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char qt1[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char on0[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char on1[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char ot0[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char ot1[TILE32];
-  __shared__ __attribute__((aligned(256))) float w0[2 * BQ];
-  __shared__ __attribute__((aligned(256))) float w1[2 * BQ];
-  // V of the workgroup's 256 keys, natural layout, for the whole launch
-  __shared__ __attribute__((aligned(1024))) unsigned char vs[KV_TILE * ROWB];
+  // One LDS array with explicit offsets.  The per-step tiles (two buffers each of Q natural for
+  // S = Q K^T, Q transposing for dK^T += Q^T dS, dO natural for dP = dO V^T, dO transposing for
+  // dV^T += dO^T P) sit in the first 64 KiB, where every operand address is one register plus an
+  // instruction offset; V of the workgroup's 256 keys (natural layout, for the whole launch) and the
+  // per-row terms follow.  The step loads are written out (dma_untracked) and waited for explicitly.
+  constexpr int QN = 0, QT = 2 * TILE32, ON = 4 * TILE32, OT = 6 * TILE32;  // + B * TILE32
+  constexpr int VS = 8 * TILE32;                 // 64 KiB
+  constexpr int WT = VS + KV_TILE * ROWB;        // + B * 256: -lse / scale, then -D, of the step's rows
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[WT + 512];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int blk = 8 * wave + i;  // rows 16 (blk / 4) .., chunks 4 (blk % 4) ..
-      dma(Vg, nv, vs + __builtin_amdgcn_readfirstlane(blk * 1024), nat_src(blk, lane, vss), sv);
+      dma_untracked(Vg, nv, lds0 + VS + blk * 1024, nat_src(blk, lane, vss), sv);
     }
   }
 
@@ -349,7 +360,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int64_t rows_total = (int64_t)f.batch * f.hq * a.q_rows;
   const uint32_t w_bytes = (uint32_t)(2 * rows_total * 4);
   const int q_lane = k_pos(kperm(l32), g);        // natural operand (query rows permuted): + 512 ks
-  const int vb_lane = k_pos(32 * wave + l32, g);  // V as B operand (lane = key): + 512 s
+  // V as B operand (lane = key): + 512 s; the per-row terms of the step (lanes read 8 g ..)
+  const unsigned char* vb_addr = smem + VS + k_pos(32 * wave + l32, g);
+  const unsigned char* w_lane = smem + WT;
   int t_lane[4];
 #pragma unroll
   for (int dvb = 0; dvb < 4; ++dvb) t_lane[dvb] = v_lane_of(lane, dvb);
@@ -416,25 +429,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     const int64_t end = c.q_row0 + c.qlen - 1;
     const uint32_t nq = (uint32_t)end * qss + ROWB, no = (uint32_t)end * oss + ROWB;
     const uint32_t sq = (uint32_t)(c.q_row0 + c.p0) * qss, so = (uint32_t)(c.q_row0 + c.p0) * oss;
-    dma(Qg, nq, (B ? qn1 : qn0) + blk_dst, qn_src, sq);
-    dma(Qg, nq, (B ? qt1 : qt0) + blk_dst, qt_src, sq);
-    dma(Og, no, (B ? on1 : on0) + blk_dst, on_src, so);
-    dma(Og, no, (B ? ot1 : ot0) + blk_dst, ot_src, so);
+    dma_untracked(Qg, nq, lds0 + QN + B * TILE32 + blk_dst, qn_src, sq);
+    dma_untracked(Qg, nq, lds0 + QT + B * TILE32 + blk_dst, qt_src, sq);
+    dma_untracked(Og, no, lds0 + ON + B * TILE32 + blk_dst, on_src, so);
+    dma_untracked(Og, no, lds0 + OT + B * TILE32 + blk_dst, ot_src, so);
     if (wave == 0 && lane < 16) {
       // lanes 0..7: -lse / scale of the 32 rows; lanes 8..15: -D
       const uint32_t row = (uint32_t)(((int64_t)b * f.hq + h) * a.q_rows + c.q_row0 + c.p0);
       const uint32_t off = (row + 4 * (lane & 7)) * 4 + (lane >= 8 ? (uint32_t)(rows_total * 4) : 0u);
-      dma(a.w, w_bytes, (unsigned char*)(B ? w1 : w0), off, 0u);
+      dma_untracked(a.w, w_bytes, lds0 + WT + B * 256, off, 0u);
     }
   };
 
   auto compute = [&](const StepCursor& c, auto bc) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    const unsigned char* qn = B ? qn1 : qn0;
-    const unsigned char* qt = B ? qt1 : qt0;
-    const unsigned char* on = B ? on1 : on0;
-    const unsigned char* ot = B ? ot1 : ot0;
-    const float* wt = B ? w1 : w0;
+    const unsigned char* qn = smem + QN + B * TILE32;
+    const unsigned char* qt = smem + QT + B * TILE32;
+    const unsigned char* on = smem + ON + B * TILE32;
+    const unsigned char* ot = smem + OT + B * TILE32;
+    const float* wt = (const float*)(w_lane + B * 256);
     // register r of lane (key l32, g) holds query row 16 (r / 8) + 8 g + r % 8 of the step
     f32x16 s, dp;
     {
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       s = mfma(*(const bf16x8*)(qn + q_lane + 512 * ks), kf[ks], s);
-      dp = mfma(*(const bf16x8*)(on + q_lane + 512 * ks), *(const bf16x8*)(vs + vb_lane + 512 * ks), dp);
+      dp = mfma(*(const bf16x8*)(on + q_lane + 512 * ks), *(const bf16x8*)(vb_addr + 512 * ks), dp);
     }
     // hide rows past the segment end and pairs past the diagonal
     const bool need_mask = (c.p0 + BQ > c.qlen) || (c.causal && kw0 + 31 - c.p0 > c.delta);
