@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "exact_long_context_amd", "csrc", "attn_fwd_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_zigzag_1m_gqa.json")
 
@@ -57,7 +58,7 @@ def workload_flop(w, ra) -> float:
     return 4.0 * w.d * w.hq * w.batch * pairs
 
 
-def time_workload(w, steps, warmup, api, torch):
+def time_workload(w, steps, warmup, api, torch, kv_splits=0):
     import synthetic
     q, k, v = synthetic.draw(w, device="cuda")
     kp = api.to_chunked(k, w.layout, w.n_chunks)
@@ -68,10 +69,12 @@ def time_workload(w, steps, warmup, api, torch):
     lse = torch.empty(qp.shape[:3], dtype=torch.float32, device="cuda")
     from exact_long_context_amd import ringattn as ra
     desc = ra.ring_desc(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=w.causal,
-                        q_chunk_first=w.query_chunks[0], out=out, lse=lse)
+                        q_chunk_first=w.query_chunks[0], out=out, lse=lse, kv_splits=kv_splits)
+    nws = ra.ra_ring_workspace_bytes(desc)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        ra.ra_ring_fwd(desc, qp, kp, vp, out, lse, stream=stream)
+        ra.ra_ring_fwd(desc, qp, kp, vp, out, lse, ws, nws, stream=stream)
     torch.cuda.synchronize()
     # events on the stream the kernel is launched on
     e0 = torch.cuda.Event(enable_timing=True)
@@ -79,7 +82,7 @@ def time_workload(w, steps, warmup, api, torch):
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
-        ra.ra_ring_fwd(desc, qp, kp, vp, out, lse, stream=stream)
+        ra.ra_ring_fwd(desc, qp, kp, vp, out, lse, ws, nws, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -120,6 +123,104 @@ def time_backward(w, steps, warmup, api, torch):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def time_memory_kernels(w, torch, reps=10):
+    """The memory-bound entry points at the workload's shapes: the layout
+    permutation of one K tensor (logical -> chunk-major and back), and state
+    initialization, finalize and the lse merge on the query chunk(s)' state.
+    Algorithmic bytes are what each call must read and write once; HIP events
+    on the launch stream around `reps` calls."""
+    from exact_long_context_amd import ringattn as ra
+    B, Hq, Hkv, d = w.batch, w.hq, w.hkv, w.d
+    rows = len(w.query_chunks) * w.chunk
+    stream = torch.cuda.current_stream()
+    res = {}
+
+    def timed(name, fn, nbytes):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "gb_per_s": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"  {name}: {ms:.3f} ms  {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM peak)")
+
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    timed("torch device copy, 1 GiB (practical ceiling)", lambda: b.copy_(a), 2 * a.numel() * 4)
+    del a, b
+    k = torch.empty(B, Hkv, w.seq, d, dtype=torch.bfloat16, device="cuda").normal_()
+    kc = torch.empty_like(k)
+    nb = 2 * k.numel() * k.element_size()
+    timed("ra_permute to chunk-major (K)", lambda: ra.ra_permute(w.layout, True, k, kc, w.n_chunks, stream), nb)
+    timed("ra_permute to logical (K)", lambda: ra.ra_permute(w.layout, False, kc, k, w.n_chunks, stream), nb)
+    del k, kc
+    torch.cuda.empty_cache()
+
+    q = torch.empty(B, Hq, rows, d, dtype=torch.bfloat16, device="cuda")
+    m = torch.empty(B, Hq, rows, dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+    o = torch.empty(B, Hq, rows, d, dtype=torch.float32, device="cuda")
+    desc = ra.attn_desc(q, q, q, ml=m, o=o)
+    n_o, n_r = o.numel() * 4, m.numel() * 4
+    timed("ra_state_init", lambda: ra.ra_state_init(desc, m, l, o, stream), n_o + 2 * n_r)
+    o.normal_()
+    l.uniform_(1.0, 2.0)
+    m.normal_()
+    out = torch.empty_like(q)
+    lse = torch.empty_like(m)
+    fdesc = ra.attn_desc(q, q, q, out=out, ml=m, o=o)
+    timed("ra_finalize", lambda: ra.ra_finalize(fdesc, m, l, o, out, lse, stream),
+          n_o + 2 * n_r + out.numel() * 2 + n_r)
+    o2 = torch.randn_like(o)
+    lse2 = torch.randn_like(m)
+    o3 = torch.empty_like(o)
+    lse3 = torch.empty_like(m)
+    mdesc = ra.ra_attn_desc()
+    mdesc.batch, mdesc.hq, mdesc.hkv, mdesc.lq, mdesc.lk, mdesc.d = B, Hq, Hq, rows, rows, d
+    mdesc.in_dtype = mdesc.out_dtype = ra.RA_F32
+    mdesc.q = mdesc.k = mdesc.v = mdesc.out = ra.strides_of(o)
+    mdesc.ml = ra.ra_strides(m.stride(0), m.stride(1), 1)
+    mdesc.o = ra.strides_of(o)
+    timed("ra_merge", lambda: ra.ra_merge(mdesc, lse, o, lse2, o2, lse3, o3, stream), 3 * (n_o + n_r))
+    del q, m, l, o, out, lse, o2, lse2, o3, lse3
+    torch.cuda.empty_cache()
+    return res
+
+
+def split_kv_report(api, torch, steps=10):
+    """One GPU's share of three workloads whose query tiles alone do not keep
+    the chip busy (few query rows, or causal work that differs between query
+    tiles): the single-pass ring forward against split-KV with the library's
+    suggested number of KV ranges (partials merged by log-sum-exp)."""
+    import synthetic
+    from exact_long_context_amd import ringattn as ra
+    res = {}
+    for name, qc in (("mha_8k", 0), ("causal_striped_128k", 15), ("causal_contig_32k", 7)):
+        w = synthetic.WORKLOADS[name].scaled(q_chunks=(qc,))
+        fl = workload_flop(w, ra)
+        q = torch.empty(w.batch, w.hq, w.chunk, w.d, dtype=torch.bfloat16)
+        k = torch.empty(w.batch, w.hkv, w.seq, w.d, dtype=torch.bfloat16)
+        hint = ra.ra_ring_kv_splits_hint(ra.ring_desc(q, k, k, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout,
+                                                      causal=w.causal, q_chunk_first=qc))
+        m1, _ = time_workload(w, steps, 2, api, torch, kv_splits=0)
+        ms, _ = time_workload(w, steps, 2, api, torch, kv_splits=hint)
+        res[f"{name} query chunk {qc}"] = {
+            "kv_splits": hint, "ms_single_pass": round(m1, 4), "ms_split": round(ms, 4),
+            "tflops_single_pass": round(fl / (m1 * 1e-3) / 1e12, 2), "tflops_split": round(fl / (ms * 1e-3) / 1e12, 2),
+            "speedup": round(m1 / ms, 3)}
+        log(f"  split-KV {name} chunk {qc}: {m1:.3f} ms -> {ms:.3f} ms with {hint} ranges ({m1 / ms:.2f}x)")
+        torch.cuda.empty_cache()
+    return res
 
 
 def balance_report(w, api, torch):
@@ -261,6 +362,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-memory", action="store_true", help="skip the memory-bound entry points")
+    ap.add_argument("--memory-only", action="store_true",
+                    help="only time the memory-bound entry points (for profiling) and exit")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time ra_ring_bwd on the workload (for profiling) and exit")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -316,6 +420,9 @@ def main():
         bms = time_backward(w, args.steps, args.warmup, api, torch)
         print(json.dumps({"backward_ms": round(bms, 3), "tflops": round(2.5 * flop / (bms * 1e-3) / 1e12, 2)}))
         return
+    if args.memory_only:
+        print(json.dumps(time_memory_kernels(w, torch, max(1, args.steps))))
+        return
     log(f"workload {w.name}: {flop:.4e} FLOP per step (causal-adjusted)")
     ms, wall = time_workload(w, args.steps, args.warmup, api, torch)
     tflops = flop / (ms * 1e-3) / 1e12
@@ -337,6 +444,10 @@ def main():
                         f"time max/min {r['ms_max_over_min']}")
                 torch.cuda.empty_cache()
 
+    split = None
+    if not args.no_others:
+        split = split_kv_report(api, torch, max(3, args.steps))
+
     backward = None
     if not args.no_backward:
         torch.cuda.empty_cache()
@@ -348,6 +459,10 @@ def main():
                     "flop_rule": "10 d per visible (query, key) pair and query head (2.5 x the forward)"}
         log(f"  backward: {bms:.3f} ms  {btf:.1f} TFLOP/s ({btf / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 peak)")
         torch.cuda.empty_cache()
+
+    memory = None
+    if not args.no_memory:
+        memory = time_memory_kernels(w, torch)
 
     cpu = None
     if not args.no_cpu:
@@ -380,6 +495,8 @@ def main():
         "cpu_baseline": cpu,
         "other_workloads": others,
         "backward": backward,
+        "split_kv_one_gpu_share": split,
+        "memory_bound_entry_points": memory,
     }
     print(json.dumps(res))
 

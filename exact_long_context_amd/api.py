@@ -27,17 +27,20 @@ def from_chunked(x: torch.Tensor, layout: str, n_chunks: int, stream=None) -> to
 
 def ring_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, seq: int, n_chunks: int, layout: str,
                  causal: bool, q_chunk_first: int = 0, out_dtype: Optional[torch.dtype] = None,
-                 return_lse: bool = True, scale: float = 0.0, stream=None):
+                 return_lse: bool = True, scale: float = 0.0, kv_splits: int = 0, stream=None):
     """All ring steps for the query chunks held in ``q`` (physical order).
 
     q: [B, Hq, n_q * L, d]; k, v: [B, Hkv, seq, d] in chunk-major order.
+    ``kv_splits`` > 1 runs the split-KV forward (workspace allocated here).
     Returns (out [B, Hq, n_q * L, d], lse [B, Hq, n_q * L] fp32 or None)."""
     B, Hq, rows, d = q.shape
     out = torch.empty(B, Hq, rows, d, dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty(B, Hq, rows, dtype=torch.float32, device=q.device) if return_lse else None
     desc = ra.ring_desc(q, k, v, seq=seq, n_chunks=n_chunks, layout=layout, causal=causal,
-                        q_chunk_first=q_chunk_first, out=out, lse=lse, scale=scale)
-    ra.ra_ring_fwd(desc, q, k, v, out, lse, stream=stream)
+                        q_chunk_first=q_chunk_first, out=out, lse=lse, scale=scale, kv_splits=kv_splits)
+    nws = ra.ra_ring_workspace_bytes(desc)
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+    ra.ra_ring_fwd(desc, q, k, v, out, lse, ws, nws, stream=stream)
     return out, lse
 
 

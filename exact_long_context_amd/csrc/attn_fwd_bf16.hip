@@ -168,6 +168,7 @@ struct TileInfo {
 // segment, the first key that needs a mask) are set up when a run starts.
 struct RunCursor {
   int32_t ri, nruns, k0, k_end, thr;
+  int32_t left;  // tiles still to produce (the workgroup's KV range)
   uint32_t so_k, so_v, nrec_k, nrec_v;
   bool done;
   __device__ __forceinline__ void load(const Run* runs, uint32_t kss, uint32_t vss, int32_t p0, bool causal) {
@@ -193,12 +194,26 @@ struct RunCursor {
       load(runs, kss, vss, p0, causal);
     }
   }
+  // Start at tile `first` of the walk (whole runs are skipped by their tile
+  // counts) and produce at most `count` tiles.
   __device__ __forceinline__ void start(const Run* runs, int32_t n, uint32_t kss, uint32_t vss, int32_t p0,
-                                        bool causal) {
-    nruns = n; ri = 0; k0 = 0; done = n <= 0;
+                                        bool causal, int32_t first, int32_t count) {
+    nruns = n; ri = 0; k0 = 0; left = count; done = n <= 0 || count <= 0;
     k_end = thr = 0;
     so_k = so_v = nrec_k = nrec_v = 0;
-    if (!done) { load(runs, kss, vss, p0, causal); skip_empty(runs, kss, vss, p0, causal); }
+    if (done) return;
+    while (ri < nruns) {
+      const int32_t nt = (__builtin_amdgcn_readfirstlane(runs[ri].k_end) + BN - 1) / BN;
+      if (first < nt) break;
+      first -= nt;
+      ++ri;
+    }
+    if (ri >= nruns) { done = true; return; }
+    load(runs, kss, vss, p0, causal);
+    k0 = first * BN;
+    so_k += (uint32_t)k0 * kss;
+    so_v += (uint32_t)k0 * vss;
+    skip_empty(runs, kss, vss, p0, causal);
   }
   __device__ __forceinline__ TileInfo tile() const {
     TileInfo t;
@@ -211,6 +226,7 @@ struct RunCursor {
     k0 += BN;
     so_k += BN * kss;
     so_v += BN * vss;
+    if (--left <= 0) { done = true; nrec_k = nrec_v = 0; return; }
     skip_empty(runs, kss, vss, p0, causal);
   }
 };
@@ -517,7 +533,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // ---- tile stream: infos of tiles n-1 .. n+2 around loop iteration n
   __syncthreads();  // run table complete
   RunCursor cur;
-  cur.start(runs, wg_p_hi < wg_p0 ? 0 : nruns, kss, vss, p0, causal);
+  {
+    const int32_t nr = wg_p_hi < wg_p0 ? 0 : nruns;
+    int32_t first = 0, count = 0x7fffffff;
+    if (a.kv_splits > 1) {
+      // this workgroup's range of the walk: tiles [T s / S, T (s + 1) / S)
+      int64_t total = 0;
+      for (int r = 0; r < nr; ++r) total += (__builtin_amdgcn_readfirstlane(runs[r].k_end) + BN - 1) / BN;
+      const int64_t tb = total * it.split / a.kv_splits, te = total * (it.split + 1) / a.kv_splits;
+      first = (int32_t)tb;
+      count = (int32_t)(te - tb);
+    }
+    cur.start(runs, nr, kss, vss, p0, causal, first, count);
+  }
   auto next_info = [&]() __attribute__((always_inline)) -> TileInfo {
     const TileInfo t = cur.tile();
     if (!cur.done) cur.advance(runs, kss, vss, p0, causal);
@@ -621,7 +649,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // ---- epilogue
   float lt = sum_pair32(l_run);
   if (my_p >= qg.len) return;
-  if (a.mode == MODE_RING) {
+  if (a.mode == MODE_RING && a.kv_splits > 1) {
+    // partial of this KV range: normalized o and natural lse
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t prow = (((int64_t)it.split * a.batch + it.b) * a.hq + h) * a.part_rows + qg.row_base + my_p;
+    float* orow = a.part_o + prow * D;
+#pragma unroll
+    for (int dvb = 0; dvb < 4; ++dvb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[dvb][r4 * 4 + e] * inv;
+        *(f32x4*)(orow + dvb * 32 + r4 * 8 + 4 * g) = v4;
+      }
+    if (g == 0) a.part_lse[prow] = lt > 0.f ? (m_ref + __log2f(lt)) * LN2 : -INFINITY;
+  } else if (a.mode == MODE_RING) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int64_t orow = (int64_t)it.b * a.out_sb + (int64_t)h * a.out_sh + (qg.row_base + my_p) * a.out_ss;
 #pragma unroll

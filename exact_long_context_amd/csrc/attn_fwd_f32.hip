@@ -58,7 +58,17 @@ __global__ __launch_bounds__(64, 1) void attn_fwd_f32_kernel(FwdArgs a) {
   const float c2 = a.scale_log2;
 
   TileCursor<BN> cur = make_cursor<BN>(a, qg, p_hi);
-  while (!cur.done) {
+  int64_t left = INT64_MAX;
+  if (a.kv_splits > 1) {
+    // this workgroup's range of the walk: tiles [T s / S, T (s + 1) / S)
+    TileCursor<BN> c = cur;
+    int64_t total = 0;
+    for (; !c.done; c.advance()) ++total;
+    const int64_t tb = total * it.split / a.kv_splits, te = total * (it.split + 1) / a.kv_splits;
+    for (int64_t i = 0; i < tb; ++i) cur.advance();
+    left = te - tb;
+  }
+  for (; !cur.done && left > 0; --left) {
     __syncthreads();
     for (int i = lane; i < BN * D; i += 64) {
       const int r = i / D, e = i - r * D;
@@ -101,7 +111,14 @@ __global__ __launch_bounds__(64, 1) void attn_fwd_f32_kernel(FwdArgs a) {
   }
 
   if (!row_ok) return;
-  if (a.mode == MODE_RING) {
+  if (a.mode == MODE_RING && a.kv_splits > 1) {
+    // partial of this KV range: normalized o and natural lse
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const int64_t prow = (((int64_t)it.split * a.batch + it.b) * a.hq + h) * a.part_rows + qg.row_base + p;
+#pragma unroll
+    for (int e = 0; e < D; ++e) a.part_o[prow * D + e] = acc[e] * inv;
+    a.part_lse[prow] = l_run > 0.f ? (m_run + log2f(l_run)) * LN2 : -INFINITY;
+  } else if (a.mode == MODE_RING) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const int64_t orow = (int64_t)it.b * a.out_sb + (int64_t)h * a.out_sh + (qg.row_base + p) * a.out_ss;
 #pragma unroll

@@ -97,6 +97,44 @@ __global__ __launch_bounds__(ROW_THREADS) void merge_kernel(RowsArgs g, const fl
   if (r.c4 == 0) lse_out[r.ml] = lse;
 }
 
+// Split-KV partials -> out, lse (the log-sum-exp associativity of the
+// lecture 013 notes, over all S partials at once).  Partial s of row
+// (b, h, p) sits at row ((s B + b) H + h) rows + p of part_lse / part_o
+// (contiguous).  Every lane of a row group reads the row's S log-sum-exps;
+// the weights are taken against their maximum, so the sum is exact up to
+// rounding in any order of s.
+__global__ __launch_bounds__(ROW_THREADS) void split_merge_kernel(RowsArgs g, int32_t S, const float* part_lse,
+                                                                  const float* part_o, void* out, int out_bf16,
+                                                                  float* lse) {
+  const RowIdx r = row_index(g);
+  if (!r.ok) return;
+  const int lpr = g.d >> 2;
+  const int64_t row = ((int64_t)blockIdx.x * ROW_THREADS + threadIdx.x) / lpr;  // (b H + h) rows + p
+  const int64_t plane = (int64_t)g.batch * g.heads * g.rows;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[s * plane + row]);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float w = expf(part_lse[s * plane + row] - M);  // exp(-inf) = 0
+      tot += w;
+      acc += *(const f32x4*)(part_o + (s * plane + row) * g.d + 4 * r.c4) * w;
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const f32x4 v = acc * inv;
+  if (out_bf16) {
+    bf16x4 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = (__bf16)v[e];
+    *(bf16x4*)((__bf16*)out + r.out) = b;
+  } else {
+    *(f32x4*)((float*)out + r.out) = v;
+  }
+  if (lse != nullptr && r.c4 == 0) lse[r.ml] = tot > 0.f ? M + logf(tot) : -INFINITY;
+}
+
 // Permutation: physical row c*L + p  <->  logical row pos(c, p).  Each thread
 // moves one UNIT-byte piece.
 template <typename UNIT>
@@ -145,6 +183,15 @@ hipError_t launch_merge(const RowsArgs& g, const float* lse_a, const float* o_a,
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g, lse_a,
                      o_a, lse_b, o_b, lse_out, o_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const RowsArgs& g, int32_t kv_splits, const float* part_lse, const float* part_o,
+                              void* out, int32_t out_bf16, float* lse, hipStream_t stream) {
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_merge_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g,
+                     kv_splits, part_lse, part_o, out, out_bf16, lse);
   return hipGetLastError();
 }
 

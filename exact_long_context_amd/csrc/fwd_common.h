@@ -15,12 +15,14 @@ struct WorkItem {
   int32_t qc_idx;          // query chunk index relative to q_first (ring) / 0 (chunk)
   int32_t qsi;             // query segment index inside the chunk
   int32_t tile;            // tile index along the segment
+  int32_t split;           // KV range (0 .. kv_splits - 1)
 };
 
 // Workgroups are numbered heaviest-first (causal work grows with the token
 // position of the rows), and, when the KV streams split evenly over the 8
 // XCDs, workgroup w lands on XCD w % 8 together with the other workgroups of
 // the same KV stream, so that tiles walking the same keys share that XCD's L2.
+// The KV ranges of one query tile (split-KV) take consecutive ranks.
 __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a, int32_t w) {
   const int32_t G = a.hq / a.hkv;
   const int32_t hg_count = G / a.heads_per_wg;
@@ -41,6 +43,8 @@ __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a, int32_t w) {
     hg = rem % hg_count;
   }
   WorkItem it;
+  it.split = r % a.kv_splits;
+  r /= a.kv_splits;
   it.b = stream / a.hkv;
   it.kvh = stream % a.hkv;
   it.hg = hg;

@@ -53,6 +53,15 @@ struct FwdArgs {
   int32_t tiles_per_seg;  // workgroups along one query segment
   int32_t xcd_swizzle;    // map workgroups so that one KV stream stays on one XCD
   int32_t n_work;         // total workgroups
+  // split-KV (MODE_RING): each query tile's KV tiles, in ring order, are cut
+  // into kv_splits consecutive ranges of (nearly) equal tile counts, one
+  // workgroup each; every range writes its normalized partial o and its
+  // natural lse (lse = -inf, o = 0 for an empty range) to part_o / part_lse,
+  // [kv_splits][B][Hq][part_rows](+[d]) fp32, row index = query buffer row.
+  int32_t kv_splits;      // 1: no split, the kernel finalizes out / lse itself
+  int32_t part_rows;
+  float* part_o;
+  float* part_lse;
 };
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
@@ -94,6 +103,12 @@ hipError_t launch_finalize(const RowsArgs& g, const float* m, const float* l, co
                            int32_t out_bf16, float* lse, hipStream_t stream);
 hipError_t launch_merge(const RowsArgs& g, const float* lse_a, const float* o_a, const float* lse_b,
                         const float* o_b, float* lse_out, float* o_out, hipStream_t stream);
+// out / lse of the rows of [B, H, rows] from kv_splits partials (the layout of
+// FwdArgs::part_o / part_lse): lse = M + ln sum_s e^(lse_s - M), M = max_s lse_s,
+// out = sum_s e^(lse_s - lse) o_s; a row with every lse_s = -inf gets out = 0,
+// lse = -inf.  g gives the out / lse strides (ml_*, out_*); lse may be null.
+hipError_t launch_split_merge(const RowsArgs& g, int32_t kv_splits, const float* part_lse, const float* part_o,
+                              void* out, int32_t out_bf16, float* lse, hipStream_t stream);
 hipError_t launch_permute(int32_t layout, int32_t to_chunked, int64_t batch_heads, int64_t seq, int32_t n_chunks,
                           int64_t row_bytes, int unit, const void* src, void* dst, hipStream_t stream);
 

@@ -105,6 +105,7 @@ void fill_common(ra::FwdArgs& a, const ra_attn_desc* d, const void* q, const voi
   a.hkv = (int32_t)d->hkv;
   a.d = (int32_t)d->d;
   a.scale_log2 = log2_scale(d);
+  a.kv_splits = 1;
 }
 
 // Work decomposition.  bf16: 8 waves of 32 rows per workgroup; the waves are
@@ -124,7 +125,7 @@ ra_status plan_launch(ra::FwdArgs& a, bool bf16, int64_t seg_len, int32_t nseg_q
   a.nseg_q = nseg_q;
   const int64_t tps = (seg_len + a.rows_per_wg - 1) / a.rows_per_wg;
   const int64_t streams = (int64_t)a.batch * a.hkv;
-  const int64_t total = streams * (G / a.heads_per_wg) * q_count * nseg_q * tps;
+  const int64_t total = streams * (G / a.heads_per_wg) * q_count * nseg_q * tps * a.kv_splits;
   if (tps > I32_MAX || total > I32_MAX) return fail(RA_ERR_INVALID_ARG, "problem too large for one launch");
   a.tiles_per_seg = (int32_t)tps;
   a.n_work = (int32_t)total;
@@ -147,7 +148,8 @@ ra_status check_kv_span(const ra_attn_desc* d, int64_t kv_rows, int64_t runs) {
 
 ra_status check_ring(const ra_ring_desc* r) {
   if (r == nullptr) return fail(RA_ERR_INVALID_ARG, "ring descriptor is NULL");
-  if (r->reserved != 0) return fail(RA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (r->kv_splits < 0 || r->kv_splits > RA_MAX_KV_SPLITS)
+    return fail(RA_ERR_INVALID_ARG, "kv_splits must be in [0, %d]", RA_MAX_KV_SPLITS);
   if (r->n_chunks < 1 || r->seq < 1) return fail(RA_ERR_INVALID_ARG, "seq and n_chunks must be >= 1");
   if (r->seq % r->n_chunks) return fail(RA_ERR_INVALID_ARG, "seq (%lld) is not a multiple of n_chunks (%d)",
                                         (long long)r->seq, r->n_chunks);
@@ -243,8 +245,10 @@ ra_status ra_merge(const ra_attn_desc* desc, const float* lse_a, const float* o_
 }
 
 size_t ra_ring_workspace_bytes(const ra_ring_desc* desc) {
-  (void)desc;
-  return 0;
+  if (desc == nullptr || desc->n_chunks < 1 || desc->kv_splits <= 1) return 0;
+  const int64_t rows = (int64_t)desc->q_chunk_count * (desc->seq / desc->n_chunks);
+  return (size_t)((int64_t)desc->kv_splits * desc->attn.batch * desc->attn.hq * rows * (desc->attn.d + 1) *
+                  (int64_t)sizeof(float));
 }
 
 ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v, void* out, float* lse,
@@ -255,8 +259,10 @@ ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, co
   if (!q || !k || !v || !out) return fail(RA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(RA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
-  if (workspace_bytes < ra_ring_workspace_bytes(desc)) return fail(RA_ERR_WORKSPACE, "workspace too small");
-  (void)workspace;
+  const size_t ws_need = ra_ring_workspace_bytes(desc);
+  if (workspace_bytes < ws_need) return fail(RA_ERR_WORKSPACE, "workspace too small (%zu bytes needed)", ws_need);
+  if (ws_need > 0 && (workspace == nullptr || !aligned16(workspace)))
+    return fail(RA_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned when kv_splits > 1");
   const ra_attn_desc* d = &desc->attn;
   ra::FwdArgs a;
   fill_common(a, d, q, k, v);
@@ -274,10 +280,54 @@ ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, co
   const int32_t nseg = ra::num_segments(desc->layout);
   const bool bf16 = d->in_dtype == RA_BF16;
   if ((st = check_kv_span(d, desc->seq, (int64_t)desc->n_chunks * nseg)) != RA_OK) return st;
+  const int32_t S = desc->kv_splits > 1 ? desc->kv_splits : 1;
+  const int64_t rows = (int64_t)desc->q_chunk_count * d->lq;
+  a.kv_splits = S;
+  if (S > 1) {
+    if (rows > I32_MAX) return fail(RA_ERR_INVALID_ARG, "query rows exceed 2^31-1");
+    a.part_rows = (int32_t)rows;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)workspace + (int64_t)S * d->batch * d->hq * rows * d->d;
+  }
   if ((st = plan_launch(a, bf16, d->lq / nseg, nseg, desc->q_chunk_count)) != RA_OK) return st;
-  return hip_status(bf16 ? ra::launch_attn_fwd_bf16(a, (hipStream_t)stream)
-                         : ra::launch_attn_fwd_f32(a, (hipStream_t)stream),
-                    "ra_ring_fwd");
+  st = hip_status(bf16 ? ra::launch_attn_fwd_bf16(a, (hipStream_t)stream)
+                       : ra::launch_attn_fwd_f32(a, (hipStream_t)stream),
+                  "ra_ring_fwd");
+  if (st != RA_OK || S == 1) return st;
+  ra::RowsArgs g;
+  g.batch = (int32_t)d->batch;
+  g.heads = (int32_t)d->hq;
+  g.rows = (int32_t)rows;
+  g.d = (int32_t)d->d;
+  g.ml_sb = d->ml.b; g.ml_sh = d->ml.h;
+  g.o_sb = g.o_sh = g.o_ss = 0;
+  g.out_sb = d->out.b; g.out_sh = d->out.h; g.out_ss = d->out.s;
+  return hip_status(ra::launch_split_merge(g, S, a.part_lse, a.part_o, out, a.out_bf16, lse, (hipStream_t)stream),
+                    "ra_ring_fwd (split merge)");
+}
+
+ra_status ra_ring_kv_splits_hint(const ra_ring_desc* desc, int32_t* splits) {
+  ra_status st = check_ring(desc);
+  if (st != RA_OK) return st;
+  if ((st = check_attn(&desc->attn)) != RA_OK) return st;
+  if (splits == nullptr) return fail(RA_ERR_INVALID_ARG, "splits is NULL");
+  const ra_attn_desc* d = &desc->attn;
+  const bool bf16 = d->in_dtype == RA_BF16;
+  ra::FwdArgs a;
+  fill_common(a, d, nullptr, nullptr, nullptr);
+  const int32_t nseg = ra::num_segments(desc->layout);
+  if ((st = plan_launch(a, bf16, d->lq / nseg, nseg, desc->q_chunk_count)) != RA_OK) return st;
+  // Below two workgroups per compute unit (a bf16 workgroup fills one; the
+  // one-wave fp32 workgroups share one), split to about four, so that short
+  // ranges also even out query tiles of different causal work; never more
+  // ranges than about one per four KV tiles of 64 keys of the sequence.
+  const int64_t enough = bf16 ? 512 : 2048;
+  int64_t s = a.n_work >= enough ? 1 : (2 * enough + a.n_work - 1) / a.n_work;
+  const int64_t cap = desc->seq / 256 > 1 ? desc->seq / 256 : 1;
+  if (s > cap) s = cap;
+  if (s > RA_MAX_KV_SPLITS) s = RA_MAX_KV_SPLITS;
+  *splits = (int32_t)(s < 1 ? 1 : s);
+  return RA_OK;
 }
 
 size_t ra_ring_bwd_workspace_bytes(const ra_ring_desc* desc) {

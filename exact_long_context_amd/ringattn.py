@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 # ---- enums (mirror include/ringattn.h)
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(5)
 RA_F32, RA_BF16 = 0, 1
+RA_MAX_KV_SPLITS = 64
 RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
 RA_FULL, RA_MASKED, RA_SKIP = 0, 1, 2
 LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED, "zigzag": RA_LAYOUT_ZIGZAG}
@@ -56,7 +57,7 @@ class ra_attn_desc(ctypes.Structure):
 class ra_ring_desc(ctypes.Structure):
     _fields_ = [("attn", ra_attn_desc), ("seq", ctypes.c_int64), ("n_chunks", ctypes.c_int32),
                 ("layout", ctypes.c_int32), ("causal", ctypes.c_int32), ("q_chunk_first", ctypes.c_int32),
-                ("q_chunk_count", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("q_chunk_count", ctypes.c_int32), ("kv_splits", ctypes.c_int32)]
 
 
 class ra_task(ctypes.Structure):
@@ -78,6 +79,7 @@ _sigs = {
     "ra_merge": (ctypes.c_int, [_P(ra_attn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ra_ring_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
     "ra_ring_fwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ra_ring_kv_splits_hint": (ctypes.c_int, [_P(ra_ring_desc), _P(ctypes.c_int32)]),
     "ra_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
     "ra_ring_bwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    ctypes.c_size_t, _vp]),
@@ -161,9 +163,11 @@ def attn_desc(q, k, v, *, out=None, ml=None, o=None, out_dtype=None, scale: floa
 
 def ring_desc(q, k, v, *, seq: int, n_chunks: int, layout, causal: bool, q_chunk_first: int = 0,
               q_chunk_count: Optional[int] = None, out=None, lse=None, out_dtype=None,
-              scale: float = 0.0) -> ra_ring_desc:
+              scale: float = 0.0, kv_splits: int = 0) -> ra_ring_desc:
     """Descriptor for :func:`ra_ring_fwd`: q holds the query chunks back to back,
-    k and v all ``n_chunks`` chunks (chunk-major physical order)."""
+    k and v all ``n_chunks`` chunks (chunk-major physical order); ``kv_splits``
+    > 1 selects the split-KV forward (its workspace from
+    :func:`ra_ring_workspace_bytes`)."""
     L = seq // n_chunks
     if q_chunk_count is None:
         q_chunk_count = q.shape[2] // L
@@ -178,7 +182,7 @@ def ring_desc(q, k, v, *, seq: int, n_chunks: int, layout, causal: bool, q_chunk
     r.causal = 1 if causal else 0
     r.q_chunk_first = q_chunk_first
     r.q_chunk_count = q_chunk_count
-    r.reserved = 0
+    r.kv_splits = kv_splits
     return r
 
 
@@ -223,6 +227,12 @@ def ra_ring_fwd(desc: ra_ring_desc, q, k, v, out, lse=None, workspace=None, work
                 stream=None):
     _check(_lib.ra_ring_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                             workspace_bytes, _stream(stream)), "ra_ring_fwd")
+
+
+def ra_ring_kv_splits_hint(desc: ra_ring_desc) -> int:
+    n = ctypes.c_int32(0)
+    _check(_lib.ra_ring_kv_splits_hint(ctypes.byref(desc), ctypes.byref(n)), "ra_ring_kv_splits_hint")
+    return n.value
 
 
 def ra_ring_bwd_workspace_bytes(desc: ra_ring_desc) -> int:

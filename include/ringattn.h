@@ -55,7 +55,10 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 1
+#define RA_ABI_VERSION 2
+
+/* Largest ra_ring_desc.kv_splits. */
+#define RA_MAX_KV_SPLITS 64
 
 typedef enum ra_status {
   RA_OK = 0,
@@ -119,7 +122,9 @@ typedef struct ra_ring_desc {
   int32_t causal;        /* 0 or 1 */
   int32_t q_chunk_first; /* first query chunk computed */
   int32_t q_chunk_count; /* number of consecutive query chunks computed */
-  int32_t reserved;      /* must be 0 */
+  int32_t kv_splits;     /* ra_ring_fwd only: 0 or 1 = one workgroup walks all KV
+                          * tiles of its query tile; 2 .. RA_MAX_KV_SPLITS = split-KV
+                          * (see ra_ring_fwd); ignored by ra_ring_bwd */
 } ra_ring_desc;
 
 /* One (query segment, KV segment) pair of the ring schedule. */
@@ -182,7 +187,9 @@ ra_status ra_merge(const ra_attn_desc* desc, const float* lse_a, const float* o_
                    const float* lse_b, const float* o_b, float* lse_out, float* o_out,
                    ra_stream stream);
 
-/* Workspace bytes ra_ring_fwd needs for this descriptor (currently 0). */
+/* Workspace bytes ra_ring_fwd needs for this descriptor: 0 without split-KV,
+ * else kv_splits * B * Hq * (q_chunk_count * L) * (d + 1) fp32 values (the
+ * partial o and lse of every KV range). */
 size_t ra_ring_workspace_bytes(const ra_ring_desc* desc);
 
 /* The whole ring: for every requested query chunk i, fold in KV chunks
@@ -191,10 +198,27 @@ size_t ra_ring_workspace_bytes(const ra_ring_desc* desc);
  * segments that are wholly in the future, mask the ones that straddle the
  * diagonal, and finalize.  One fused launch: the state stays on chip from the
  * first step to the last.  out: desc.attn.out_dtype, strides desc.attn.out;
- * lse may be NULL.  Rows that see no key give out = 0, lse = -inf. */
+ * lse may be NULL.  Rows that see no key give out = 0, lse = -inf.
+ * Split-KV (desc.kv_splits = S > 1; for few query rows, or causal work that
+ * differs much between query tiles): the KV tiles one query tile visits, in
+ * ring order, are cut into S consecutive ranges of nearly equal tile counts,
+ * each walked by its own workgroup into a normalized partial (o_s, lse_s) in
+ * the workspace, and a second kernel merges them with the log-sum-exp
+ * associativity of the lecture 013 notes (lse = M + ln sum_s e^(lse_s - M), out =
+ * sum_s e^(lse_s - lse) o_s, M = max lse_s; the pairwise merge of ra_merge
+ * folded over all S at once).  Same result up to rounding.  workspace: device
+ * memory of ra_ring_workspace_bytes(desc) bytes, 16-byte aligned, used during
+ * the call only (may be NULL when that is 0). */
 ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v,
                       void* out, float* lse, void* workspace, size_t workspace_bytes,
                       ra_stream stream);
+
+/* Host only.  A kv_splits value for ra_ring_fwd on this descriptor: 1 when
+ * the query tiles alone give every compute unit two workgroups or more, else
+ * enough KV ranges for about four per compute unit (at most
+ * RA_MAX_KV_SPLITS, and at most one per 256 keys of the sequence).
+ * desc.kv_splits itself is not read. */
+ra_status ra_ring_kv_splits_hint(const ra_ring_desc* desc, int32_t* splits);
 
 /* Workspace bytes ra_ring_bwd needs for this descriptor: two fp32 values per
  * (batch, query head, query row) of the requested query chunks. */

@@ -42,7 +42,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(ra.ra_attn_desc) == 6 * 8 + 2 * 4 + 6 * 24 + 4 + 4
     assert ctypes.sizeof(ra.ra_ring_desc) == ctypes.sizeof(ra.ra_attn_desc) + 8 + 6 * 4
     assert ctypes.sizeof(ra.ra_task) == 6 * 4 + 8 + 2 * 4
-    assert ra.ra_abi_version() == 1
+    assert ra.ra_abi_version() == 2
     assert ra.ra_status_str(0) == "ok" and ra.ra_status_str(3) == "workspace too small"
 
 
@@ -192,23 +192,41 @@ def test_finalize_merge_state_validation():
         ra.RA_ERR_UNSUPPORTED
 
 
-def _ring(layout="zigzag", S=256, N=4, causal=1, first=0, count=4, lq=None, lk=None, reserved=0, ws=0, **kw):
+def _ring_desc(layout="zigzag", S=256, N=4, causal=1, first=0, count=4, lq=None, lk=None, kv_splits=0, **kw):
     r = ra.ra_ring_desc()
     L = S // N if N > 0 else 0
     r.attn = _adesc(lq=lq if lq is not None else max(L, 1), lk=lk if lk is not None else max(L, 1), **kw)
     r.seq, r.n_chunks = S, N
     r.layout = ra.LAYOUTS.get(layout, 9) if isinstance(layout, str) else layout
-    r.causal, r.q_chunk_first, r.q_chunk_count, r.reserved = causal, first, count, reserved
-    return ra._lib.ra_ring_fwd(ctypes.byref(r), P, P, P, P, None, None, ws, None)
+    r.causal, r.q_chunk_first, r.q_chunk_count, r.kv_splits = causal, first, count, kv_splits
+    return r
+
+
+def _ring(ws=0, wsp=None, **kw):
+    r = _ring_desc(**kw)
+    return ra._lib.ra_ring_fwd(ctypes.byref(r), P, P, P, P, None, wsp, ws, None)
 
 
 @pytest.mark.parametrize("kw", [
     dict(S=250, N=4), dict(N=0), dict(layout=9), dict(S=12, N=4, count=4),  # odd L for zig-zag
     dict(causal=2), dict(first=3, count=2), dict(first=-1), dict(count=0), dict(lq=32), dict(lk=128),
-    dict(reserved=5), dict(hq=4, hkv=3), dict(S=1 << 32, N=1, lq=1, lk=1),
+    dict(kv_splits=-1), dict(kv_splits=ra.RA_MAX_KV_SPLITS + 1), dict(hq=4, hkv=3),
+    dict(S=1 << 32, N=1, lq=1, lk=1),
 ])
 def test_ring_fwd_rejects_bad_descriptors(kw):
     assert _ring(**kw) == ra.RA_ERR_INVALID_ARG
+
+
+def test_ring_split_kv_workspace():
+    # partial o (d floats) and lse (1 float) per split and (b, query head, row)
+    for S, count in ((0, 4), (1, 4), (2, 4), (5, 1), (ra.RA_MAX_KV_SPLITS, 2)):
+        r = _ring_desc(S=256, N=4, count=count, B=2, hq=4, hkv=2, kv_splits=S)
+        want = 0 if S <= 1 else S * 2 * 4 * (count * 64) * (128 + 1) * 4
+        assert ra.ra_ring_workspace_bytes(r) == want
+    need = ra.ra_ring_workspace_bytes(_ring_desc(kv_splits=3))
+    assert _ring(kv_splits=3, ws=need - 1, wsp=P) == ra.RA_ERR_WORKSPACE
+    assert _ring(kv_splits=3, ws=need, wsp=None) == ra.RA_ERR_INVALID_ARG
+    assert _ring(kv_splits=3, ws=need, wsp=P + 8) == ra.RA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw", [
@@ -242,3 +260,27 @@ def test_permute_and_positions_validation():
         ra.ra_layout_positions("zigzag", 12, 4, 0)
     with pytest.raises(ra.RingAttnError):
         ra.ra_layout_positions("striped", 16, 4, 4)
+
+
+def test_ring_kv_splits_hint():
+    """More KV ranges when there are few query tiles, none when the query
+    tiles already give every compute unit two workgroups; bounded by
+    RA_MAX_KV_SPLITS and by seq / 256."""
+    def hint(**kw):
+        return ra.ra_ring_kv_splits_hint(_ring_desc(**kw))
+    # 1M-token zig-zag share: 4096 workgroups, no split
+    assert hint(S=1 << 20, N=32, count=1, hq=32, hkv=8) == 1
+    # one 2048-row chunk of 8 MHA heads: 64 workgroups -> 16 ranges
+    assert hint(layout="contiguous", S=8192, N=4, count=1, hq=8, hkv=8, causal=0) == 16
+    # tiny sequences: at most one range per 256 keys
+    assert hint(layout="contiguous", S=512, N=4, count=1, hq=1, hkv=1) == 2
+    assert hint(layout="contiguous", S=64, N=4, count=1, hq=1, hkv=1) == 1
+    # one 8192-row striped chunk of 8 MHA heads: 256 workgroups -> 4 ranges
+    assert hint(layout="striped", S=1 << 17, N=16, first=15, count=1, hq=8, hkv=8) == 4
+    # the last 4096-row contiguous chunk of 32 MHA heads: 512 workgroups, no split
+    assert hint(layout="contiguous", S=1 << 15, N=8, first=7, count=1, hq=32, hkv=32) == 1
+    assert 1 <= hint(layout="striped", S=1 << 17, N=16, count=1, hq=1, hkv=1) <= ra.RA_MAX_KV_SPLITS
+    r = _ring_desc(kv_splits=-3)
+    with pytest.raises(ra.RingAttnError):
+        ra.ra_ring_kv_splits_hint(r)
+
