@@ -197,6 +197,55 @@ def time_memory_kernels(w, torch, reps=10):
     return res
 
 
+def time_stepwise(w, steps, warmup, api, torch):
+    """The workload's query chunk as one device of the ring runs it: state
+    init, one ra_ring_step per ring step (each given only its KV chunk, a view
+    of the resident chunk-major K / V standing for the received buffer, the
+    running state in HBM between steps), finalize.  HIP events on the launch
+    stream around `steps` passes."""
+    import synthetic
+    from exact_long_context_amd import ringattn as ra
+    assert len(w.query_chunks) == 1
+    i = w.query_chunks[0]
+    q, k, v = synthetic.draw(w, device="cuda")
+    kp = api.to_chunked(k, w.layout, w.n_chunks)
+    vp = api.to_chunked(v, w.layout, w.n_chunks)
+    del k, v
+    L = w.chunk
+    st = api.ChunkState(q)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    adesc = ra.attn_desc(q, kp, vp, ml=st.m, o=st.o)
+    fdesc = ra.attn_desc(q, q, q, out=out, ml=st.m, o=st.o)
+    views = []
+    for t in range(w.n_chunks):
+        j = (i - t) % w.n_chunks
+        kj, vj = kp[:, :, j * L:(j + 1) * L], vp[:, :, j * L:(j + 1) * L]
+        d = ra.ring_desc(q, kj, vj, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=w.causal,
+                         q_chunk_first=i, q_chunk_count=1, lse=st.m)
+        d.attn.o = ra.strides_of(st.o)
+        views.append((t, d, kj, vj))
+    stream = torch.cuda.current_stream()
+
+    def one_pass():
+        ra.ra_state_init(adesc, st.m, st.l, st.o, stream)
+        for t, d, kj, vj in views:
+            ra.ra_ring_step(d, t, q, kj, vj, st.m, st.l, st.o, stream)
+        ra.ra_finalize(fdesc, st.m, st.l, st.o, out, lse, stream)
+
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def split_kv_report(api, torch, steps=10):
     """One GPU's share of three workloads whose query tiles alone do not keep
     the chip busy (few query rows, or causal work that differs between query
@@ -445,8 +494,16 @@ def main():
                 torch.cuda.empty_cache()
 
     split = None
+    stepwise = None
     if not args.no_others:
         split = split_kv_report(api, torch, max(3, args.steps))
+        sms = time_stepwise(w, max(2, args.steps // 3), 1, api, torch)
+        stepwise = {"entry_point": "ra_ring_step", "steps_per_pass": w.n_chunks, "ms": round(sms, 3),
+                    "tflops": round(flop / (sms * 1e-3) / 1e12, 2), "ms_fused": round(ms, 3),
+                    "stepwise_over_fused": round(sms / ms, 4)}
+        log(f"  step by step (ra_ring_step x {w.n_chunks}): {sms:.3f} ms  {stepwise['tflops']} TFLOP/s "
+            f"({sms / ms:.3f} x the fused launch)")
+        torch.cuda.empty_cache()
 
     backward = None
     if not args.no_backward:
@@ -496,6 +553,7 @@ def main():
         "other_workloads": others,
         "backward": backward,
         "split_kv_one_gpu_share": split,
+        "ring_step_one_gpu_share": stepwise,
         "memory_bound_entry_points": memory,
     }
     print(json.dumps(res))

@@ -101,6 +101,31 @@ def finalize(st: ChunkState, q, out_dtype: Optional[torch.dtype] = None, stream=
     return out, lse
 
 
+def ring_step(st: ChunkState, q, k_chunk, v_chunk, *, step: int, seq: int, n_chunks: int, layout: str,
+              causal: bool, q_chunk: int, scale: float = 0.0, stream=None) -> ChunkState:
+    """Ring step ``step`` of query chunk ``q_chunk``: ``k_chunk`` / ``v_chunk``
+    hold KV chunk (q_chunk - step) mod N only, [B, Hkv, L, d]."""
+    desc = ra.ring_desc(q, k_chunk, v_chunk, seq=seq, n_chunks=n_chunks, layout=layout, causal=causal,
+                        q_chunk_first=q_chunk, q_chunk_count=1, lse=st.m, scale=scale)
+    desc.attn.o = ra.strides_of(st.o)
+    ra.ra_ring_step(desc, step, q, k_chunk, v_chunk, st.m, st.l, st.o, stream)
+    return st
+
+
+def ring_forward_stepwise(q, k, v, *, seq: int, n_chunks: int, layout: str, causal: bool, q_chunk: int,
+                          out_dtype: Optional[torch.dtype] = None, scale: float = 0.0, stream=None):
+    """The ring of one query chunk as a device runs it: state init, the N steps
+    in ring order, each given only its KV chunk (a view of the chunk-major k, v
+    here, standing for the received buffer), then finalize."""
+    L = seq // n_chunks
+    st = state_init(q, k, stream)
+    for t in range(n_chunks):
+        j = (q_chunk - t) % n_chunks
+        ring_step(st, q, k[:, :, j * L:(j + 1) * L], v[:, :, j * L:(j + 1) * L], step=t, seq=seq,
+                  n_chunks=n_chunks, layout=layout, causal=causal, q_chunk=q_chunk, scale=scale, stream=stream)
+    return finalize(st, q, out_dtype, stream)
+
+
 def merge(lse_a, o_a, lse_b, o_b, lse_out=None, o_out=None, stream=None):
     """Log-sum-exp merge of two normalized fp32 partials [B, H, L] / [B, H, L, d]."""
     lse_out = torch.empty_like(lse_a) if lse_out is None else lse_out

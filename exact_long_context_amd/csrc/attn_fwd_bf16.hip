@@ -132,12 +132,15 @@ __device__ __forceinline__ Run make_run(const FwdArgs& a, const QGeom& qg, int32
     e.kv_len = a.lk;
     dl = a.delta;
   } else {
+    // MODE_RING: run r is segment r % nseg of step r / nseg; MODE_STEP: the
+    // segments of the one step, in a buffer that holds only its KV chunk
     const int32_t nseg = num_segments(a.layout);
-    const int32_t t = nseg == 2 ? (r >> 1) : r;
+    const bool one_step = a.mode == MODE_STEP;
+    const int32_t t = one_step ? a.step : (nseg == 2 ? (r >> 1) : r);
     const int32_t sb = nseg == 2 ? (r & 1) : 0;
     const int32_t j = ring_kv_chunk(qg.qchunk, t, a.n_chunks);
     const Segment ks = segment_l(a.layout, a.lq, a.n_chunks, j, sb);
-    e.kv_row = j * a.lq + ks.row0;
+    e.kv_row = (one_step ? 0 : j * a.lq) + ks.row0;
     e.kv_len = ks.len;
     dl = a.causal ? pair_delta(qg.seg, ks) : 0;
   }
@@ -231,8 +234,8 @@ struct RunCursor {
   }
 };
 
-// EXACT: track the exact running maximum (chunk mode hands back the state
-// relative to it); ring mode needs only the reference.
+// EXACT: track the exact running maximum (chunk and step modes hand back the
+// state relative to it); ring mode needs only the reference.
 template <bool EXACT>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // four distinct arrays, so that the compiler can tell the buffer being
@@ -259,7 +262,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int wg_p0 = it.tile * a.rows_per_wg;
   const int p0 = __builtin_amdgcn_readfirstlane(wg_p0 + (wave / HP) * WAVE_ROWS);  // first row of this wave
   const int wg_p_hi = min(wg_p0 + a.rows_per_wg, qg.len) - 1;
-  const int nruns = a.mode == MODE_CHUNK ? 1 : a.n_chunks * num_segments(a.layout);
+  const int nruns = a.mode == MODE_CHUNK ? 1
+                    : (a.mode == MODE_STEP ? 1 : a.n_chunks) * num_segments(a.layout);
   for (int r = tid; r < nruns; r += NTHREADS) runs[r] = make_run(a, qg, wg_p_hi, r);
   const int my_p = p0 + l32;                        // this lane's query row
 
@@ -284,13 +288,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   f32x16 acc[4];  // acc[dvb]: O^T[dv = dvb*32 + 8(r/4) + 4g + r%4][query my_p]
 #pragma unroll
   for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] = f32x16{};
-  if (a.mode == MODE_CHUNK && my_p < qg.len) {
-    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + my_p;
+  if (a.mode != MODE_RING && my_p < qg.len) {
+    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + my_p;
     const float mv = a.m[mi];
     m_ref = mv == -INFINITY ? -INFINITY : mv * LOG2E;
     m_max = m_ref;
     l_run = g == 0 ? a.l[mi] : 0.f;
-    const float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)my_p * a.o_ss;
+    const float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + my_p) * a.o_ss;
 #pragma unroll
     for (int dvb = 0; dvb < 4; ++dvb)
 #pragma unroll
@@ -689,15 +693,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       a.lse[li] = lt > 0.f ? (m_ref + __log2f(lt)) * LN2 : -INFINITY;
     }
   } else {
-    // hand back the state relative to the exact running maximum
+    // chunk / step mode: hand back the state relative to the exact running maximum
     const float f = (m_max == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_max);
     lt *= f;
-    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + my_p;
+    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + my_p;
     if (g == 0) {
       a.m[mi] = m_max == -INFINITY ? -INFINITY : m_max * LN2;
       a.l[mi] = lt;
     }
-    float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)my_p * a.o_ss;
+    float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + my_p) * a.o_ss;
 #pragma unroll
     for (int dvb = 0; dvb < 4; ++dvb)
 #pragma unroll
@@ -714,7 +718,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.n_work <= 0) return hipSuccess;
-  if (a.mode == MODE_CHUNK)
+  if (a.mode != MODE_RING)
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3(a.n_work), dim3(NTHREADS), 0, stream, a);
   else
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(a.n_work), dim3(NTHREADS), 0, stream, a);

@@ -46,12 +46,12 @@ __global__ __launch_bounds__(64, 1) void attn_fwd_f32_kernel(FwdArgs a) {
     q[e] = row_ok ? Qg[(qg.row_base + p) * a.q_ss + e] : 0.f;
     acc[e] = 0.f;
   }
-  if (a.mode == MODE_CHUNK && row_ok) {
-    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + p;
+  if (a.mode != MODE_RING && row_ok) {
+    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + p;
     const float mv = a.m[mi];
     m_run = mv == -INFINITY ? -INFINITY : mv * LOG2E;
     l_run = a.l[mi];
-    const float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
+    const float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + p) * a.o_ss;
 #pragma unroll
     for (int e = 0; e < D; ++e) acc[e] = orow[e];
   }
@@ -131,10 +131,10 @@ __global__ __launch_bounds__(64, 1) void attn_fwd_f32_kernel(FwdArgs a) {
       a.lse[li] = l_run > 0.f ? (m_run + log2f(l_run)) * LN2 : -INFINITY;
     }
   } else {
-    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + p;
+    const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + p;
     a.m[mi] = m_run == -INFINITY ? -INFINITY : m_run * LN2;
     a.l[mi] = l_run;
-    float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
+    float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + p) * a.o_ss;
 #pragma unroll
     for (int e = 0; e < D; ++e) orow[e] = acc[e];
   }

@@ -99,7 +99,7 @@ __device__ __forceinline__ QGeom query_geom(const FwdArgs& a, const WorkItem& it
 
 // Walks the KV tiles a workgroup must visit, in ring order: step t visits KV
 // chunk (q - t) mod N, its segments in row order, keys ascending inside a
-// segment.  Tiles wholly in the future of the workgroup's last row are never
+// segment (step mode: only step a.step, in a buffer holding that chunk).  Tiles wholly in the future of the workgroup's last row are never
 // produced; segment pairs classified SKIP produce no tile at all.
 template <int BN>
 struct TileCursor {
@@ -111,6 +111,7 @@ struct TileCursor {
   int32_t p_hi;          // last valid query row of the workgroup in the segment
   int32_t lk;            // chunk mode: key rows
   int64_t delta_chunk;   // chunk mode: causal offset
+  int32_t t_first, t_end;  // ring steps walked
   // moving
   int32_t t, sb;         // ring step, KV segment index
   int32_t k0;            // first key of the tile, relative to the segment
@@ -129,7 +130,7 @@ struct TileCursor {
     } else {
       const int32_t j = ring_kv_chunk(qchunk, t, n);
       const Segment ks = segment_l(layout, L, n, j, sb);
-      kv_row = (int64_t)j * L + ks.row0;
+      kv_row = (mode == MODE_STEP ? 0 : (int64_t)j * L) + ks.row0;
       kv_len = ks.len;
       dl = causal ? pair_delta(qseg, ks) : 0;
     }
@@ -144,17 +145,16 @@ struct TileCursor {
   }
 
   __device__ __forceinline__ void skip_empty() {
-    const int32_t nsteps = mode == MODE_CHUNK ? 1 : n;
     while (!done && k0 >= k_end) {
       if (++sb >= nseg) { sb = 0; ++t; }
-      if (t >= nsteps) { done = true; break; }
+      if (t >= t_end) { done = true; break; }
       k0 = 0;
       load_run();
     }
   }
 
   __device__ __forceinline__ void start() {
-    t = 0; sb = 0; k0 = 0; done = false;
+    t = t_first; sb = 0; k0 = 0; done = false;
     load_run();
     skip_empty();
   }
@@ -180,6 +180,8 @@ __device__ __forceinline__ TileCursor<BN> make_cursor(const FwdArgs& a, const QG
   c.p_hi = p_hi;
   c.lk = a.lk;
   c.delta_chunk = a.delta;
+  c.t_first = a.mode == MODE_STEP ? a.step : 0;
+  c.t_end = a.mode == MODE_CHUNK ? 1 : (a.mode == MODE_STEP ? a.step + 1 : a.n_chunks);
   c.start();
   return c;
 }

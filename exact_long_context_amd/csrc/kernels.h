@@ -6,11 +6,13 @@
 
 namespace ra {
 
-// Arguments of the fused attention-forward kernels.  One launch covers either
-// a single chunk update with the running state in HBM (mode CHUNK) or the
-// whole ring for a range of query chunks with the state kept on chip and the
-// output finalized at the end (mode RING).
-enum FwdMode : int32_t { MODE_CHUNK = 0, MODE_RING = 1 };
+// Arguments of the fused attention-forward kernels.  One launch covers a
+// single chunk update with the running state in HBM (mode CHUNK), the whole
+// ring for a range of query chunks with the state kept on chip and the output
+// finalized at the end (mode RING), or one ring step of one query chunk with
+// that step's KV chunk in its own buffer and the running state in HBM (mode
+// STEP: what each device of a ring runs when a KV chunk arrives).
+enum FwdMode : int32_t { MODE_CHUNK = 0, MODE_RING = 1, MODE_STEP = 2 };
 
 // The bf16 kernel keeps the table of the KV segments one workgroup walks in
 // LDS; a call may cover at most this many (ring steps x segments per chunk).
@@ -23,7 +25,7 @@ struct FwdArgs {
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
-  // running state (MODE_CHUNK): m, l [B, Hq, Lq]; o [B, Hq, Lq, d]
+  // running state (MODE_CHUNK, MODE_STEP): m, l [B, Hq, Lq]; o [B, Hq, Lq, d]
   float* m;
   float* l;
   float* o;
@@ -37,11 +39,14 @@ struct FwdArgs {
   int32_t batch, hq, hkv, d;
   int32_t mode;
   int32_t causal;
-  // ring geometry (MODE_RING): chunk length L, layout, N chunks
+  // ring geometry (MODE_RING, MODE_STEP): chunk length L, layout, N chunks;
+  // MODE_STEP computes ring step `step` of query chunk q_first (q_count = 1)
+  // and its K / V rows are those of KV chunk (q_first - step) mod N only
   int32_t layout;
   int32_t n_chunks;
   int64_t seq;
   int32_t q_first, q_count;
+  int32_t step;
   // chunk geometry (MODE_CHUNK): lq query rows, lk key rows, one offset
   int32_t lq, lk;
   int64_t delta;

@@ -306,6 +306,53 @@ ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, co
                     "ra_ring_fwd (split merge)");
 }
 
+ra_status ra_ring_step(const ra_ring_desc* desc, int32_t step, const void* q, const void* k, const void* v, float* m,
+                       float* l, float* o, ra_stream stream) {
+  ra_status st = check_ring(desc);
+  if (st != RA_OK) return st;
+  if ((st = check_attn(&desc->attn)) != RA_OK) return st;
+  if (desc->q_chunk_count != 1) return fail(RA_ERR_INVALID_ARG, "ra_ring_step takes one query chunk (q_chunk_count = 1)");
+  if (step < 0 || step >= desc->n_chunks) return fail(RA_ERR_INVALID_ARG, "step %d out of [0, n_chunks)", step);
+  if (!q || !k || !v || !m || !l || !o) return fail(RA_ERR_INVALID_ARG, "q, k, v, m, l and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(RA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  const ra_attn_desc* d = &desc->attn;
+  const int32_t nseg = ra::num_segments(desc->layout);
+  const int32_t qc = desc->q_chunk_first;
+  const int32_t j = ra::ring_kv_chunk(qc, step, desc->n_chunks);
+  // nothing to do when every (query segment, KV segment) pair of the step is
+  // wholly in the future
+  if (desc->causal) {
+    bool any = false;
+    for (int qs = 0; qs < nseg; ++qs)
+      for (int ks = 0; ks < nseg; ++ks) {
+        const ra::Segment a = ra::segment(desc->layout, desc->seq, desc->n_chunks, qc, qs);
+        const ra::Segment b = ra::segment(desc->layout, desc->seq, desc->n_chunks, j, ks);
+        if (ra::pair_kind(ra::pair_delta(a, b), a.len, b.len) != RA_SKIP) any = true;
+      }
+    if (!any) return RA_OK;
+  }
+  const bool bf16 = d->in_dtype == RA_BF16;
+  if ((st = check_kv_span(d, d->lk, nseg)) != RA_OK) return st;
+  ra::FwdArgs a;
+  fill_common(a, d, q, k, v);
+  a.m = m; a.l = l; a.o = o;
+  a.mode = ra::MODE_STEP;
+  a.causal = desc->causal;
+  a.layout = desc->layout;
+  a.n_chunks = desc->n_chunks;
+  a.seq = desc->seq;
+  a.q_first = qc;
+  a.q_count = 1;
+  a.step = step;
+  a.lq = (int32_t)d->lq;
+  a.lk = (int32_t)d->lk;
+  if ((st = plan_launch(a, bf16, d->lq / nseg, nseg, 1)) != RA_OK) return st;
+  return hip_status(bf16 ? ra::launch_attn_fwd_bf16(a, (hipStream_t)stream)
+                         : ra::launch_attn_fwd_f32(a, (hipStream_t)stream),
+                    "ra_ring_step");
+}
+
 ra_status ra_ring_kv_splits_hint(const ra_ring_desc* desc, int32_t* splits) {
   ra_status st = check_ring(desc);
   if (st != RA_OK) return st;

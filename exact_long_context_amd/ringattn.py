@@ -80,6 +80,7 @@ _sigs = {
     "ra_ring_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
     "ra_ring_fwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ra_ring_kv_splits_hint": (ctypes.c_int, [_P(ra_ring_desc), _P(ctypes.c_int32)]),
+    "ra_ring_step": (ctypes.c_int, [_P(ra_ring_desc), ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ra_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
     "ra_ring_bwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    ctypes.c_size_t, _vp]),
@@ -227,6 +228,11 @@ def ra_ring_fwd(desc: ra_ring_desc, q, k, v, out, lse=None, workspace=None, work
                 stream=None):
     _check(_lib.ra_ring_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                             workspace_bytes, _stream(stream)), "ra_ring_fwd")
+
+
+def ra_ring_step(desc: ra_ring_desc, step: int, q, k, v, m, l, o, stream=None):
+    _check(_lib.ra_ring_step(ctypes.byref(desc), int(step), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(l), _ptr(o),
+                             _stream(stream)), "ra_ring_step")
 
 
 def ra_ring_kv_splits_hint(desc: ra_ring_desc) -> int:

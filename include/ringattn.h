@@ -213,6 +213,24 @@ ra_status ra_ring_fwd(const ra_ring_desc* desc, const void* q, const void* k, co
                       void* out, float* lse, void* workspace, size_t workspace_bytes,
                       ra_stream stream);
 
+/* One ring step of one query chunk, as a device of the ring runs it when a
+ * KV chunk arrives (ring_attention_forward on the youngju.dev page: step t of
+ * query chunk i folds in KV chunk j = (i - t) mod N; the glossary page's
+ * four-device simulation): skip the segment pairs wholly in the future, mask
+ * the ones on the diagonal, fold the rest into the running (m, l, o), which
+ * stays in device memory between steps.  Starting from ra_state_init and
+ * ending with ra_finalize, the N steps in any order give ra_ring_fwd's result
+ * (the order changes rounding only).
+ * desc: q_chunk_count must be 1, the query chunk is q_chunk_first; kv_splits
+ * is not used.  q: that chunk's rows [B, Hq, L, d] (strides desc.attn.q);
+ * k, v: the rows of KV chunk j only, [B, Hkv, L, d] (strides desc.attn.k /
+ * desc.attn.v), in the chunk's physical row order; m, l: [B, Hq, L] fp32
+ * (strides desc.attn.ml); o: [B, Hq, L, d] fp32 (strides desc.attn.o), all
+ * read and overwritten (m natural, relative to which l and o are kept, as
+ * ra_chunk_fwd).  A step with nothing visible returns without a launch. */
+ra_status ra_ring_step(const ra_ring_desc* desc, int32_t step, const void* q, const void* k, const void* v,
+                       float* m, float* l, float* o, ra_stream stream);
+
 /* Host only.  A kv_splits value for ra_ring_fwd on this descriptor: 1 when
  * the query tiles alone give every compute unit two workgroups or more, else
  * enough KV ranges for about four per compute unit (at most

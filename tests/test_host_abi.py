@@ -284,3 +284,28 @@ def test_ring_kv_splits_hint():
     with pytest.raises(ra.RingAttnError):
         ra.ra_ring_kv_splits_hint(r)
 
+
+
+def _step(step, qp=P, kp=P, vp=P, mp=P, lp=P, op=P, **kw):
+    r = _ring_desc(**kw)
+    return ra._lib.ra_ring_step(ctypes.byref(r), step, qp, kp, vp, mp, lp, op, None)
+
+
+def test_ring_step_validation():
+    one = dict(count=1)
+    assert _step(0, count=2) == ra.RA_ERR_INVALID_ARG          # one query chunk per call
+    assert _step(-1, **one) == ra.RA_ERR_INVALID_ARG
+    assert _step(4, **one) == ra.RA_ERR_INVALID_ARG            # N = 4 steps
+    assert _step(0, kp=None, **one) == ra.RA_ERR_INVALID_ARG
+    assert _step(0, mp=None, **one) == ra.RA_ERR_INVALID_ARG
+    assert _step(0, op=P + 4, **one) == ra.RA_ERR_INVALID_ARG
+    assert _step(0, layout=9, **one) == ra.RA_ERR_INVALID_ARG
+    assert _step(0, d=64, **one) == ra.RA_ERR_UNSUPPORTED
+    assert ra._lib.ra_ring_step(None, 0, P, P, P, P, P, P, None) == ra.RA_ERR_INVALID_ARG
+
+
+def test_ring_step_wholly_future_is_a_no_op():
+    # contiguous causal, query chunk 1 of 4: steps 2 and 3 bring KV chunks 3
+    # and 2, wholly after it; the call returns OK without launching anything
+    for t in (2, 3):
+        assert _step(t, layout="contiguous", first=1, count=1) == ra.RA_OK
