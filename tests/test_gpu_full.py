@@ -118,3 +118,46 @@ def test_full_backward_zigzag_1m_sampled():
     err = max_abs(dq[0, hs, rs].cpu().double().numpy(), want)
     print(f"  dq max-abs error on {len(samples)} rows {err:.2e} (magnitude {np.abs(want).max():.2e})", flush=True)
     assert err <= TOL["bf16"]
+
+
+def _check_sampled(w, out, lse, qp, k, v, n, seed):
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    samples = sample_rows(w, n, seed=seed)
+    ref, ref_lse = oracle_sampled(w, samples, qp, k, v, causal=w.causal)
+    hs = torch.tensor([h for h, _ in samples], device=out.device)
+    rs = torch.tensor([r for _, r in samples], device=out.device)
+    e_out = max_abs(out[0, hs, rs].float().cpu().double().numpy(), ref)
+    e_lse = max_abs(lse[0, hs, rs].cpu().double().numpy(), ref_lse)
+    print(f"  max-abs out {e_out:.3e} lse {e_lse:.3e}", flush=True)
+    assert e_out <= TOL["bf16"] and e_lse <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,qc", [("mha_8k", 0), ("causal_striped_128k", 15)])
+def test_full_split_kv_one_chunk_sampled(name, qc):
+    """Split-KV in the configuration the bench times: one query chunk of the
+    workload with the library's suggested number of KV ranges."""
+    from exact_long_context_amd import ringattn as ra
+    w = synthetic.WORKLOADS[name].scaled(q_chunks=(qc,))
+    q = torch.empty(w.batch, w.hq, w.chunk, w.d, dtype=torch.bfloat16)
+    kk = torch.empty(w.batch, w.hkv, w.seq, w.d, dtype=torch.bfloat16)
+    splits = ra.ra_ring_kv_splits_hint(ra.ring_desc(q, kk, kk, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout,
+                                                    causal=w.causal, q_chunk_first=qc))
+    assert splits > 1
+    print(f"case full split-KV {name} chunk {qc}, {splits} ranges", flush=True)
+    qp, kp, vp, q, k, v = physical_inputs(w)
+    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=w.causal,
+                                q_chunk_first=qc, kv_splits=splits)
+    torch.cuda.synchronize()
+    _check_sampled(w, out, lse, qp, k, v, 512, seed=qc + 7)
+
+
+def test_full_ring_step_zigzag_1m_sampled():
+    """The 1M-token zig-zag share run step by step as the bench times it: state
+    init, 32 ra_ring_step calls each given only its KV chunk, finalize."""
+    w = synthetic.WORKLOADS["zigzag_1m_gqa"]
+    print("case full ring step zigzag_1m_gqa", flush=True)
+    qp, kp, vp, q, k, v = physical_inputs(w)
+    out, lse = api.ring_forward_stepwise(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout,
+                                         causal=True, q_chunk=w.query_chunks[0])
+    torch.cuda.synchronize()
+    _check_sampled(w, out, lse, qp, k, v, 512, seed=1234)
