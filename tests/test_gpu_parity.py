@@ -352,3 +352,34 @@ def test_strided_inputs():
     torch.cuda.synchronize()
     ref, ref_lse = OA.attention_reference(q.cpu(), k.cpu(), v.cpu(), causal=True)
     assert max_abs(out, ref) <= TOL["bf16"] and max_abs(lse, ref_lse) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_strided_inputs_and_outputs(splits):
+    """Strided q / k / v / out views and a padded lse, single-pass and split-KV
+    (the split merge writes through the same out / lse strides)."""
+    print(f"case strided out splits={splits}", flush=True)
+    B, S, H, d, N = 2, 768, 4, 128, 4
+    base = [synthetic.normal_draw((B, S, H, d), 11 + i, dtype=torch.bfloat16, device=DEV) for i in range(3)]
+    q, k, v = (t.transpose(1, 2) for t in base)
+    out_base = torch.full((B, S, H, d), 7.0, dtype=torch.float32, device=DEV)
+    out = out_base.transpose(1, 2)
+    lse_base = torch.full((B, H, S + 40), 7.0, dtype=torch.float32, device=DEV)
+    lse = lse_base[:, :, :S]
+    desc = ra.ring_desc(q, k, v, seq=S, n_chunks=N, layout="striped", causal=True, out=out, lse=lse,
+                        kv_splits=splits)
+    nws = ra.ra_ring_workspace_bytes(desc)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+    qp = api.to_chunked(q.contiguous(), "striped", N)
+    kp = api.to_chunked(k.contiguous(), "striped", N)
+    vp = api.to_chunked(v.contiguous(), "striped", N)
+    # physical inputs copied back into strided views of the same shape
+    qs, ks, vs = (torch.empty_like(b).transpose(1, 2) for b in base)
+    qs.copy_(qp), ks.copy_(kp), vs.copy_(vp)
+    ra.ra_ring_fwd(desc, qs, ks, vs, out, lse, ws, nws)
+    torch.cuda.synchronize()
+    pos = torch.from_numpy(OL.all_positions("striped", S, N))
+    ref, ref_lse = OA.attention_reference(qp.cpu(), k.cpu(), v.cpu(), causal=True, q_pos=pos.numpy(),
+                                          k_pos=np.arange(S))
+    assert max_abs(out, ref) <= TOL["bf16"] and max_abs(lse, ref_lse) <= TOL["bf16"]
+    assert torch.all(lse_base[:, :, S:] == 7.0)  # padding untouched
