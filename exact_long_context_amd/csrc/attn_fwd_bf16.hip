@@ -23,8 +23,9 @@
 // handed back by the chunk entry point.
 //
 // Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the SIMDs
-// pairwise.  Each wave alternates two kinds of slot, separated by workgroup
-// barriers, with group B one slot behind group A:
+// pairwise.  Each wave alternates two kinds of slot, with group B one slot
+// behind group A (one workgroup barrier per iteration, after the second slot;
+// within an iteration the hardware arbitrates between the pair):
 //   matrix slot : S^T of tile n and O^T += V^T P^T of tile n-1 (32 MFMA,
 //                 operand reads issued ahead of use)
 //   vector slot : mask / max / exponentials / row sum of the tile whose S^T
@@ -584,18 +585,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(0) is in LDS
   __syncthreads();
 
-  // Barrier between slots.  Not __syncthreads(): its release fence would wait
-  // for the staging loads in flight (they write LDS); the staging is waited
-  // for explicitly before the second barrier of an iteration instead.  LDS
-  // reads may stay in flight across it (group B's first operands): no buffer
-  // read in an iteration is written before the next iteration.
+  // Barrier at the end of an iteration.  Not __syncthreads(): its release
+  // fence would also wait for LDS reads in flight; the staging loads are
+  // waited for explicitly just before it.  No buffer read in an iteration is
+  // written before the next one, so a barrier between the two slots is not
+  // needed (and measured 0.9 % slower).
   auto slot_barrier = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
 
-  // Loop iteration n (two slots, a barrier after each):
+  // Loop iteration n (two slots, a barrier after the second):
   //   slot 1: A matrix (QK(n), PV(n-1))  |  B vector (softmax(n-1))
   //   slot 2: A vector (softmax(n))  |  B matrix (QK(n), PV(n-1))
   // Staging of K(n+1) into K buffer (n+1) % 2 and of V(n) into V buffer n % 2
@@ -629,7 +630,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       // complete since the previous iteration
       first_reads(kbc, vbc);
     }
-    slot_barrier();
     if (grp == 0) {
       if (t0.valid()) softmax_tile(t0, nothing);
     } else {
