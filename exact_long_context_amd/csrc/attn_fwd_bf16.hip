@@ -601,7 +601,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   //   slot 2: A vector (softmax(n))  |  B matrix (QK(n), PV(n-1))
   // Staging of K(n+1) into K buffer (n+1) % 2 and of V(n) into V buffer n % 2
   // is issued in slot 1 by both groups, one 1 KiB block per wave at a time
-  // (group A between its last MFMA pairs, group B spread over its softmax),
+  // (group A after every other MFMA pair of the second half of its matrix
+  // slot, group B spread over its softmax),
   // and waited for at the end of slot 2; neither buffer is read in iteration n.
   auto iteration = [&](auto qc) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;   // n % 4
@@ -614,14 +615,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     auto stage = [&](int j) __attribute__((always_inline)) {
       stage_block(j, t1, P ? kbuf0 : kbuf1, t0, P ? vbuf1 : vbuf0);
     };
-    auto stage_last4 = [&](int i) __attribute__((always_inline)) {
-      if (i >= 12) stage(i - 12);
+    auto stage_late = [&](int i) __attribute__((always_inline)) {
+      if (i >= 8 && (i & 1) == 0) stage((i - 8) >> 1);
     };
     auto nothing = [&](int) __attribute__((always_inline)) {};
     const std::false_type read_first{};
     const std::true_type prefetched{};
     if (grp == 0) {
-      matrix_slot(kbc, vbc, stage_last4, read_first);
+      matrix_slot(kbc, vbc, stage_late, read_first);
     } else {
       // also on tile -1 (iteration 0), where S^T = -inf makes it a no-op
       // that leaves P^T = 0: the staging blocks are issued from inside it
