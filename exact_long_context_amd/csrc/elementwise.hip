@@ -1,11 +1,13 @@
 // Memory-bound kernels of the library: state initialization, finalize, the
 // log-sum-exp merge of two partials, and the layout permutation.
 //
-// Row kernels give each row to a group of d/4 consecutive lanes, each lane
-// moving 16 bytes of the row, so a wave touches 64 consecutive 16-byte pieces
-// of the row-major tensors (coalesced) and reads every per-row scalar once per
-// lane group, before any lane of that group writes (which makes the in-place
-// merge safe).
+// Row kernels give each row to a group of d/8 consecutive lanes, each lane
+// moving 8 fp32 values (two 16-byte pieces) of the row, so a wave touches
+// 2 KiB of consecutive fp32 state (coalesced) and reads every per-row scalar
+// once per lane group, before any lane of that group writes (which makes the
+// in-place merge safe).  Eight values per lane measured 10 % faster than four
+// for finalize and state init; finalize also streams o with non-temporal
+// loads (8 % faster; non-temporal stores slowed merge and state init).
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -16,6 +18,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int ROW_THREADS = 256;
 
@@ -24,11 +27,11 @@ struct RowIdx {
   int64_t ml;   // index into m / l / lse
   int64_t o;    // index of this lane's 4 floats in o
   int64_t out;  // index of this lane's 4 elements in out
-  int c4;       // which 4-element piece
+  int c4;       // which 8-element piece
 };
 
 __device__ __forceinline__ RowIdx row_index(const RowsArgs& g) {
-  const int lpr = g.d >> 2;  // lanes per row
+  const int lpr = g.d >> 3;  // lanes per row
   const int64_t t = (int64_t)blockIdx.x * ROW_THREADS + threadIdx.x;
   const int64_t row = t / lpr;
   RowIdx r;
@@ -39,8 +42,8 @@ __device__ __forceinline__ RowIdx row_index(const RowsArgs& g) {
   const int64_t p = row - bh * g.rows;
   const int64_t b = bh / g.heads, h = bh - b * g.heads;
   r.ml = b * g.ml_sb + h * g.ml_sh + p;
-  r.o = b * g.o_sb + h * g.o_sh + p * g.o_ss + 4 * r.c4;
-  r.out = b * g.out_sb + h * g.out_sh + p * g.out_ss + 4 * r.c4;
+  r.o = b * g.o_sb + h * g.o_sh + p * g.o_ss + 8 * r.c4;
+  r.out = b * g.out_sb + h * g.out_sh + p * g.out_ss + 8 * r.c4;
   return r;
 }
 
@@ -52,6 +55,7 @@ __global__ __launch_bounds__(ROW_THREADS) void state_init_kernel(RowsArgs g, flo
     l[r.ml] = 0.f;
   }
   *(f32x4*)(o + r.o) = f32x4{0.f, 0.f, 0.f, 0.f};
+  *(f32x4*)(o + r.o + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 __global__ __launch_bounds__(ROW_THREADS) void finalize_kernel(RowsArgs g, const float* m, const float* l,
@@ -62,14 +66,16 @@ __global__ __launch_bounds__(ROW_THREADS) void finalize_kernel(RowsArgs g, const
   const float lv = l[r.ml];
   const bool seen = lv > 0.f;
   const float inv = seen ? 1.f / lv : 0.f;
-  const f32x4 v = *(const f32x4*)(o + r.o) * inv;
+  const f32x4 v = __builtin_nontemporal_load((const f32x4*)(o + r.o)) * inv;
+  const f32x4 w = __builtin_nontemporal_load((const f32x4*)(o + r.o + 4)) * inv;
   if (out_bf16) {
-    bf16x4 b;
+    bf16x8 b;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) b[e] = (__bf16)v[e];
-    *(bf16x4*)((__bf16*)out + r.out) = b;
+    for (int e = 0; e < 4; ++e) { b[e] = (__bf16)v[e]; b[4 + e] = (__bf16)w[e]; }
+    *(bf16x8*)((__bf16*)out + r.out) = b;
   } else {
     *(f32x4*)((float*)out + r.out) = v;
+    *(f32x4*)((float*)out + r.out + 4) = w;
   }
   if (lse != nullptr && r.c4 == 0) lse[r.ml] = seen ? m[r.ml] + logf(lv) : -INFINITY;
 }
@@ -80,8 +86,8 @@ __global__ __launch_bounds__(ROW_THREADS) void merge_kernel(RowsArgs g, const fl
   const RowIdx r = row_index(g);
   if (!r.ok) return;
   const float la = lse_a[r.ml], lb = lse_b[r.ml];
-  const f32x4 va = *(const f32x4*)(o_a + r.o);
-  const f32x4 vb = *(const f32x4*)(o_b + r.o);
+  const f32x4 va = *(const f32x4*)(o_a + r.o), va2 = *(const f32x4*)(o_a + r.o + 4);
+  const f32x4 vb = *(const f32x4*)(o_b + r.o), vb2 = *(const f32x4*)(o_b + r.o + 4);
   const float M = fmaxf(la, lb);
   float lse, wa, wb;
   if (M == -INFINITY) {
@@ -94,6 +100,7 @@ __global__ __launch_bounds__(ROW_THREADS) void merge_kernel(RowsArgs g, const fl
     wb = eb / tot;
   }
   *(f32x4*)(o_out + r.o) = va * wa + vb * wb;
+  *(f32x4*)(o_out + r.o + 4) = va2 * wa + vb2 * wb;
   if (r.c4 == 0) lse_out[r.ml] = lse;
 }
 
@@ -108,29 +115,32 @@ __global__ __launch_bounds__(ROW_THREADS) void split_merge_kernel(RowsArgs g, in
                                                                   float* lse) {
   const RowIdx r = row_index(g);
   if (!r.ok) return;
-  const int lpr = g.d >> 2;
+  const int lpr = g.d >> 3;
   const int64_t row = ((int64_t)blockIdx.x * ROW_THREADS + threadIdx.x) / lpr;  // (b H + h) rows + p
   const int64_t plane = (int64_t)g.batch * g.heads * g.rows;
   float M = -INFINITY;
   for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[s * plane + row]);
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, acc2 = acc;
   float tot = 0.f;
   if (M != -INFINITY) {
     for (int s = 0; s < S; ++s) {
       const float w = expf(part_lse[s * plane + row] - M);  // exp(-inf) = 0
       tot += w;
-      acc += *(const f32x4*)(part_o + (s * plane + row) * g.d + 4 * r.c4) * w;
+      const float* src = part_o + (s * plane + row) * g.d + 8 * r.c4;
+      acc += *(const f32x4*)src * w;
+      acc2 += *(const f32x4*)(src + 4) * w;
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  const f32x4 v = acc * inv;
+  const f32x4 v = acc * inv, v2 = acc2 * inv;
   if (out_bf16) {
-    bf16x4 b;
+    bf16x8 b;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) b[e] = (__bf16)v[e];
-    *(bf16x4*)((__bf16*)out + r.out) = b;
+    for (int e = 0; e < 4; ++e) { b[e] = (__bf16)v[e]; b[4 + e] = (__bf16)v2[e]; }
+    *(bf16x8*)((__bf16*)out + r.out) = b;
   } else {
     *(f32x4*)((float*)out + r.out) = v;
+    *(f32x4*)((float*)out + r.out + 4) = v2;
   }
   if (lse != nullptr && r.c4 == 0) lse[r.ml] = tot > 0.f ? M + logf(tot) : -INFINITY;
 }
@@ -161,7 +171,7 @@ inline unsigned blocks_for(int64_t threads, int per) { return (unsigned)((thread
 }  // namespace
 
 hipError_t launch_state_init(const RowsArgs& g, float* m, float* l, float* o, hipStream_t stream) {
-  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 3);
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(state_init_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g, m,
                      l, o);
@@ -170,7 +180,7 @@ hipError_t launch_state_init(const RowsArgs& g, float* m, float* l, float* o, hi
 
 hipError_t launch_finalize(const RowsArgs& g, const float* m, const float* l, const float* o, void* out,
                            int32_t out_bf16, float* lse, hipStream_t stream) {
-  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 3);
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(finalize_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g, m,
                      l, o, out, out_bf16, lse);
@@ -179,7 +189,7 @@ hipError_t launch_finalize(const RowsArgs& g, const float* m, const float* l, co
 
 hipError_t launch_merge(const RowsArgs& g, const float* lse_a, const float* o_a, const float* lse_b,
                         const float* o_b, float* lse_out, float* o_out, hipStream_t stream) {
-  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 3);
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g, lse_a,
                      o_a, lse_b, o_b, lse_out, o_out);
@@ -188,7 +198,7 @@ hipError_t launch_merge(const RowsArgs& g, const float* lse_a, const float* o_a,
 
 hipError_t launch_split_merge(const RowsArgs& g, int32_t kv_splits, const float* part_lse, const float* part_o,
                               void* out, int32_t out_bf16, float* lse, hipStream_t stream) {
-  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 2);
+  const int64_t threads = (int64_t)g.batch * g.heads * g.rows * (g.d >> 3);
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(split_merge_kernel, dim3(blocks_for(threads, ROW_THREADS)), dim3(ROW_THREADS), 0, stream, g,
                      kv_splits, part_lse, part_o, out, out_bf16, lse);

@@ -72,7 +72,7 @@ ra_status check_attn(const ra_attn_desc* d) {
   return RA_OK;
 }
 
-// The row kernels give every row d/4 lanes; d is one of 16..128 here.
+// The row kernels give every row d/8 lanes; d is one of 16..128 here.
 ra::RowsArgs rows_args(const ra_attn_desc* d) {
   ra::RowsArgs g;
   g.batch = (int32_t)d->batch;
