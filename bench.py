@@ -414,6 +414,10 @@ def main():
     ap.add_argument("--no-memory", action="store_true", help="skip the memory-bound entry points")
     ap.add_argument("--memory-only", action="store_true",
                     help="only time the memory-bound entry points (for profiling) and exit")
+    ap.add_argument("--split-only", action="store_true",
+                    help="only run the split-KV report on the one-chunk shares (for profiling) and exit")
+    ap.add_argument("--stepwise-only", action="store_true",
+                    help="only time the workload step by step through ra_ring_step (for profiling) and exit")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time ra_ring_bwd on the workload (for profiling) and exit")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -471,6 +475,13 @@ def main():
         return
     if args.memory_only:
         print(json.dumps(time_memory_kernels(w, torch, max(1, args.steps))))
+        return
+    if args.split_only:
+        print(json.dumps(split_kv_report(api, torch, max(1, args.steps))))
+        return
+    if args.stepwise_only:
+        sms = time_stepwise(w, max(1, args.steps), args.warmup, api, torch)
+        print(json.dumps({"stepwise_ms": round(sms, 3), "tflops": round(flop / (sms * 1e-3) / 1e12, 2)}))
         return
     log(f"workload {w.name}: {flop:.4e} FLOP per step (causal-adjusted)")
     ms, wall = time_workload(w, args.steps, args.warmup, api, torch)
