@@ -320,18 +320,24 @@ ra_status ra_ring_step(const ra_ring_desc* desc, int32_t step, const void* q, co
   const int32_t nseg = ra::num_segments(desc->layout);
   const int32_t qc = desc->q_chunk_first;
   const int32_t j = ra::ring_kv_chunk(qc, step, desc->n_chunks);
-  // nothing to do when every (query segment, KV segment) pair of the step is
-  // wholly in the future
+  // Query segments with a visible key in this step.  Nothing to do when there
+  // is none; in the zig-zag layout the late segment always sees the step's
+  // chunk and the early one only when that chunk is not later than its own,
+  // so otherwise only the late segment's workgroups are launched (the work
+  // decomposition puts the late segment first).
+  bool seg_live[2] = {true, true};
   if (desc->causal) {
-    bool any = false;
-    for (int qs = 0; qs < nseg; ++qs)
+    for (int qs = 0; qs < nseg; ++qs) {
+      seg_live[qs] = false;
+      const ra::Segment a = ra::segment(desc->layout, desc->seq, desc->n_chunks, qc, qs);
       for (int ks = 0; ks < nseg; ++ks) {
-        const ra::Segment a = ra::segment(desc->layout, desc->seq, desc->n_chunks, qc, qs);
         const ra::Segment b = ra::segment(desc->layout, desc->seq, desc->n_chunks, j, ks);
-        if (ra::pair_kind(ra::pair_delta(a, b), a.len, b.len) != RA_SKIP) any = true;
+        if (ra::pair_kind(ra::pair_delta(a, b), a.len, b.len) != RA_SKIP) seg_live[qs] = true;
       }
-    if (!any) return RA_OK;
+    }
+    if (!seg_live[0] && (nseg == 1 || !seg_live[1])) return RA_OK;
   }
+  const int32_t nseg_launch = (nseg == 2 && !seg_live[0]) ? 1 : nseg;
   const bool bf16 = d->in_dtype == RA_BF16;
   if ((st = check_kv_span(d, d->lk, nseg)) != RA_OK) return st;
   ra::FwdArgs a;
@@ -347,7 +353,7 @@ ra_status ra_ring_step(const ra_ring_desc* desc, int32_t step, const void* q, co
   a.step = step;
   a.lq = (int32_t)d->lq;
   a.lk = (int32_t)d->lk;
-  if ((st = plan_launch(a, bf16, d->lq / nseg, nseg, 1)) != RA_OK) return st;
+  if ((st = plan_launch(a, bf16, d->lq / nseg, nseg_launch, 1)) != RA_OK) return st;
   return hip_status(bf16 ? ra::launch_attn_fwd_bf16(a, (hipStream_t)stream)
                          : ra::launch_attn_fwd_f32(a, (hipStream_t)stream),
                     "ra_ring_step");
