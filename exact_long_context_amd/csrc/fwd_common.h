@@ -99,8 +99,9 @@ __device__ __forceinline__ QGeom query_geom(const FwdArgs& a, const WorkItem& it
 
 // Walks the KV tiles a workgroup must visit, in ring order: step t visits KV
 // chunk (q - t) mod N, its segments in row order, keys ascending inside a
-// segment (step mode: only step a.step, in a buffer holding that chunk).  Tiles wholly in the future of the workgroup's last row are never
-// produced; segment pairs classified SKIP produce no tile at all.
+// segment (step mode: only step a.step, in a buffer holding that chunk).
+// Tiles wholly in the future of the workgroup's last row are never produced;
+// segment pairs classified SKIP produce no tile at all.
 template <int BN>
 struct TileCursor {
   // fixed
