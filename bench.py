@@ -30,6 +30,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "exact_long_context_amd", "csrc", "attn_fwd_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_zigzag_1m_gqa.json")
+TRAFFIC_WORKLOAD = "zigzag_1m_gqa"   # the workload the counter runs were taken on
 
 
 def log(*a):
@@ -350,10 +351,10 @@ def cpu_baseline(w, flop_total):
                       f"{flop_total / (flop / dt) / 3600:.1f} h at this rate"}
 
 
-def traffic_record():
+def traffic_record(workload):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the kernel source as it is now."""
-    if not os.path.exists(TRAFFIC_FILE):
+    were taken on this workload and on the kernel source as it is now."""
+    if workload != TRAFFIC_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
     h = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
@@ -490,7 +491,7 @@ def main():
 
     others = {}
     if not args.no_others:
-        for name in ("mha_8k", "mha_8k_sharp", "causal_contig_32k", "causal_striped_128k"):
+        for name in ("mha_8k", "mha_8k_sharp", "causal_contig_32k", "causal_striped_128k", "usp_1m_share"):
             wo = synthetic.WORKLOADS[name]
             fo = workload_flop(wo, ra)
             mo, _ = time_workload(wo, max(3, args.steps), 2, api, torch)
@@ -559,7 +560,7 @@ def main():
                    "flop_per_step": flop, "pct_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS * 100, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_record()},
+                     "traffic": traffic_record(w.name)},
         "cpu_baseline": cpu,
         "other_workloads": others,
         "backward": backward,

@@ -17,12 +17,16 @@ Workloads (all batch 1, i.i.d. N(0, 1) entries):
 * ``zigzag_1m_gqa``  -- 32 query heads sharing 8 KV heads, 1048576 tokens in
   32 zig-zag chunks of 32768; one query chunk is computed against all 32 KV
   chunks.
+* ``usp_1m_share``   -- the same layer as one GPU's share under the hybrid of
+  the youngju.dev page (``hybrid_ulysses_ring_attention``) with a head
+  all-to-all over 8 GPUs and a ring over 4: 4 query heads sharing 1 KV head,
+  1048576 tokens in 4 zig-zag chunks of 262144; one query chunk against all 4.
 
 Draw recipe for the bf16 workloads: a ``torch.Generator`` on the requested
 device seeded with the workload's seed; fp32 N(0,1) samples in the order q, k,
 v; each tensor drawn in its logical token order ``[B, H, S, d]`` and rounded to
-bf16 (round-to-nearest-even).  For ``zigzag_1m_gqa`` only the rows of the
-computed query chunk are drawn for q, in that chunk's own row order
+bf16 (round-to-nearest-even).  For ``zigzag_1m_gqa`` and ``usp_1m_share``
+only the rows of the computed query chunk are drawn for q, in that chunk's own row order
 ``[B, Hq, L, d]``; k and v cover all S tokens.
 """
 from __future__ import annotations
@@ -68,6 +72,7 @@ WORKLOADS = {
     "causal_contig_32k": Workload("causal_contig_32k", 1, 32, 32, 32768, 8, 128, "bf16", True, "contiguous", 3),
     "causal_striped_128k": Workload("causal_striped_128k", 1, 8, 8, 131072, 16, 128, "bf16", True, "striped", 4),
     "zigzag_1m_gqa": Workload("zigzag_1m_gqa", 1, 32, 8, 1048576, 32, 128, "bf16", True, "zigzag", 5, q_chunks=(0,)),
+    "usp_1m_share": Workload("usp_1m_share", 1, 4, 1, 1048576, 4, 128, "bf16", True, "zigzag", 6, q_chunks=(0,)),
 }
 
 

@@ -42,7 +42,7 @@ def test_full_noncausal_8k_every_element(name):
 
 
 @pytest.mark.parametrize("name,n", [("causal_contig_32k", 1024), ("causal_striped_128k", 1024),
-                                    ("zigzag_1m_gqa", 768)])
+                                    ("zigzag_1m_gqa", 768), ("usp_1m_share", 512)])
 def test_full_causal_sampled_rows(name, n):
     w = synthetic.WORKLOADS[name]
     print(f"case full {name} ({n} sampled rows)", flush=True)
