@@ -57,8 +57,10 @@ def ring_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     for t, ref in ((dq, q), (dk, k), (dv, v)):
-        assert t.stride() == ref.stride(), "gradients take the strides of their inputs: pass contiguous tensors"
-    assert dout.stride() == out.stride() and dout.dtype == q.dtype
+        if t.stride() != ref.stride():
+            raise ValueError("gradients take the strides of their inputs: pass contiguous q, k, v")
+    if dout.stride() != out.stride() or dout.dtype != q.dtype:
+        raise ValueError("dout must have the strides of out and the dtype of q")
     desc = ra.ring_desc(q, k, v, seq=seq, n_chunks=n_chunks, layout=layout, causal=causal,
                         q_chunk_first=q_chunk_first, out=out, lse=lse, scale=scale)
     need = ra.ra_ring_bwd_workspace_bytes(desc)
@@ -138,8 +140,10 @@ def merge(lse_a, o_a, lse_b, o_b, lse_out=None, o_out=None, stream=None):
     desc.ml = ra.ra_strides(lse_a.stride(0), lse_a.stride(1), 1)
     desc.o = ra.strides_of(o_a)
     for t in (lse_b, lse_out):
-        assert t.stride() == lse_a.stride()
+        if t.stride() != lse_a.stride():
+            raise ValueError("lse tensors must share strides")
     for t in (o_b, o_out):
-        assert t.stride() == o_a.stride()
+        if t.stride() != o_a.stride():
+            raise ValueError("o tensors must share strides")
     ra.ra_merge(desc, lse_a, o_a, lse_b, o_b, lse_out, o_out, stream)
     return lse_out, o_out
