@@ -410,7 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="zigzag_1m_gqa")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads, the split-KV report and the step-by-step timing")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-memory", action="store_true", help="skip the memory-bound entry points")
     ap.add_argument("--memory-only", action="store_true",
