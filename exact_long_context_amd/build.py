@@ -29,7 +29,7 @@ EXTRA_FLAGS = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_bwd_bf16.hip": ["
 
 ARCH = "gfx950"
 # packed fp32 VALU forms are disabled for every HIP object (see the design notes)
-COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
+COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-I", INCLUDE, "-I", CSRC]
 

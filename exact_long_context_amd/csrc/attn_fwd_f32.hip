@@ -41,6 +41,9 @@ __global__ __launch_bounds__(64, 1) void attn_fwd_f32_kernel(FwdArgs a) {
 
   float q[D], acc[D];
   float m_run = -INFINITY, l_run = 0.f;
+  // chunk / step modes: the incoming m (natural) and its base-2 image; a row
+  // whose maximum does not move hands m back unchanged, not re-rounded
+  float m_in = -INFINITY, m_in2 = -INFINITY;
 #pragma unroll
   for (int e = 0; e < D; ++e) {
     q[e] = row_ok ? Qg[(qg.row_base + p) * a.q_ss + e] : 0.f;
@@ -48,8 +51,8 @@ __global__ __launch_bounds__(64, 1) void attn_fwd_f32_kernel(FwdArgs a) {
   }
   if (a.mode != MODE_RING && row_ok) {
     const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + p;
-    const float mv = a.m[mi];
-    m_run = mv == -INFINITY ? -INFINITY : mv * LOG2E;
+    m_in = a.m[mi];
+    m_run = m_in2 = m_in == -INFINITY ? -INFINITY : m_in * LOG2E;
     l_run = a.l[mi];
     const float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + p) * a.o_ss;
 #pragma unroll
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(64, 1) void attn_fwd_f32_kernel(FwdArgs a) {
     }
   } else {
     const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + p;
-    a.m[mi] = m_run == -INFINITY ? -INFINITY : m_run * LN2;
+    a.m[mi] = m_run == m_in2 ? m_in : m_run * LN2;
     a.l[mi] = l_run;
     float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + p) * a.o_ss;
 #pragma unroll

@@ -166,6 +166,19 @@ ra_status check_ring(const ra_ring_desc* r) {
   return RA_OK;
 }
 
+// Descriptor checks of the backward (before any pointer is looked at).
+ra_status check_bwd_desc(const ra_ring_desc* desc) {
+  ra_status st = check_ring(desc);
+  if (st != RA_OK) return st;
+  if ((st = check_attn(&desc->attn)) != RA_OK) return st;
+  const ra_attn_desc* d = &desc->attn;
+  if (d->in_dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward needs bf16 inputs (d = 128)");
+  // dout is bf16 and read with the strides of out, in 16-byte pieces
+  if (d->out.b % 8 || d->out.h % 8 || d->out.s % 8)
+    return fail(RA_ERR_INVALID_ARG, "out strides must be multiples of 8 elements (dout is bf16 and shares them)");
+  return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,11 +405,9 @@ size_t ra_ring_bwd_workspace_bytes(const ra_ring_desc* desc) {
 ra_status ra_ring_bwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, float* dq, float* dk, float* dv, void* workspace,
                       size_t workspace_bytes, ra_stream stream) {
-  ra_status st = check_ring(desc);
+  ra_status st = check_bwd_desc(desc);
   if (st != RA_OK) return st;
-  if ((st = check_attn(&desc->attn)) != RA_OK) return st;
   const ra_attn_desc* d = &desc->attn;
-  if (d->in_dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward needs bf16 inputs (d = 128)");
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
     return fail(RA_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk, dv and workspace must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||

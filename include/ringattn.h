@@ -162,7 +162,8 @@ ra_status ra_state_init(const ra_attn_desc* desc, float* m, float* l, float* o, 
  * q: [B, Hq, lq, d]; k, v: [B, Hkv, lk, d] (desc.in_dtype, strides desc.q/k/v).
  * m, l, o: running state, read and written in place (fp32).
  * causal / causal_delta: see the conventions above.  A row that sees no key
- * is left unchanged. */
+ * is left unchanged, bit for bit; a row whose maximum does not grow gets its
+ * m back bit for bit. */
 ra_status ra_chunk_fwd(const ra_attn_desc* desc, const void* q, const void* k, const void* v,
                        float* m, float* l, float* o, int64_t causal_delta, int32_t causal,
                        ra_stream stream);
@@ -253,7 +254,8 @@ size_t ra_ring_bwd_workspace_bytes(const ra_ring_desc* desc);
  * contributions of all its query heads.
  * Inputs (device): q, k, v as for ra_ring_fwd; out (the forward's output,
  * desc.attn.out_dtype, strides desc.attn.out); dout (bf16, strides
- * desc.attn.out); lse (natural, fp32, strides desc.attn.ml) as ra_ring_fwd
+ * desc.attn.out, which must then be multiples of 8 elements whatever
+ * out_dtype is); lse (natural, fp32, strides desc.attn.ml) as ra_ring_fwd
  * writes it.
  * Outputs (device, fp32, overwritten): dq with the element strides of q;
  * dk and dv with the element strides of k and v, for all n_chunks chunks:
@@ -271,15 +273,24 @@ ra_status ra_ring_bwd(const ra_ring_desc* desc, const void* q, const void* k, co
                       size_t workspace_bytes, ra_stream stream);
 
 /* Host only.  pos[p] = global token position of row p of chunk `chunk`
- * (p = 0 .. seq/n_chunks - 1) under `layout`.  pos is host memory of
- * seq / n_chunks entries. */
+ * (p = 0 .. seq/n_chunks - 1) under `layout`: the token split of the
+ * "Context Parallelism" page (each GPU takes a chunk of consecutive tokens;
+ * causal imbalance, where the zig-zag mix of early and late tokens is
+ * proposed without a formula) and the striped assignment of the glossary page
+ * "Ring Attention" (how it works: tokens spread evenly over the devices); the
+ * maps are those of ra_layout above.  pos is host memory of seq / n_chunks
+ * entries. */
 ra_status ra_layout_positions(int32_t layout, int64_t seq, int32_t n_chunks, int32_t chunk,
                               int64_t* pos);
 
 /* Host only.  The schedule that ra_ring_fwd runs for query chunk q_chunk, in
  * ring order: per step, every (query segment, KV segment) pair with its
  * causal offset and kind (SKIP pairs are listed; ra_ring_fwd does not run
- * them).  Writes up to `capacity` entries to the host array `tasks` and the
+ * them).  The order is the ring order of ring_attention_forward on the
+ * youngju.dev page (step t visits KV chunk (q_chunk - t) mod N) and the kinds
+ * are the three cases of its ring_attention_causal_step listing (a future
+ * block is skipped, the diagonal block is masked, a past block is computed
+ * in full).  Writes up to `capacity` entries to the host array `tasks` and the
  * total count to *n_tasks; returns RA_ERR_INVALID_ARG if capacity is too
  * small (n_tasks still receives the count). */
 ra_status ra_ring_schedule(const ra_ring_desc* desc, int32_t q_chunk, ra_task* tasks,
@@ -287,7 +298,9 @@ ra_status ra_ring_schedule(const ra_ring_desc* desc, int32_t q_chunk, ra_task* t
 
 /* Reorder rows between logical token order and the chunk-major physical
  * order of `layout` (a gather or scatter along the row dimension; a bit-exact
- * copy).  src and dst are contiguous [batch, heads, seq, d] of `dtype` and
+ * copy): the split of the sequence over the devices that the data collator of
+ * the youngju.dev page (LongContextDataCollator) and the token chunks of the
+ * "Context Parallelism" page perform, with the row maps of ra_layout.  src and dst are contiguous [batch, heads, seq, d] of `dtype` and
  * must not overlap.  to_chunked != 0: dst row c*L + p = src row pos(c, p);
  * to_chunked == 0: the inverse. */
 ra_status ra_permute(int32_t layout, int32_t to_chunked, int64_t batch, int64_t heads, int64_t seq,

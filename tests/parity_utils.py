@@ -17,16 +17,30 @@ def query_rows_positions(w: synthetic.Workload) -> np.ndarray:
     return np.concatenate([OL.chunk_positions(w.layout, w.seq, w.n_chunks, c) for c in w.query_chunks])
 
 
+def gather_chunked(w: synthetic.Workload, x: torch.Tensor) -> torch.Tensor:
+    """Logical [B, H, S, d] -> chunk-major order by a plain index gather over
+    the oracle's own position maps (no library code involved)."""
+    pos = torch.from_numpy(OL.all_positions(w.layout, w.seq, w.n_chunks)).to(x.device)
+    return x.index_select(2, pos).contiguous()
+
+
 def physical_inputs(w: synthetic.Workload, device="cuda"):
     """(q_phys, k_phys, v_phys, q_logical_or_rows, k_log, v_log) on the device.
 
-    The chunk-major reordering is done by the library's permutation kernel and
-    checked bit-exactly against an index gather in the tests."""
+    K and V are reordered to chunk-major order by the library's permutation
+    kernel (they feed only the GPU path; the oracle reads the logical k, v).
+    The query rows, which both sides read, come from a plain index gather over
+    the oracle's position maps; the library's permutation of q is checked
+    against that gather bit for bit here."""
     from exact_long_context_amd import api
     q, k, v = synthetic.draw(w, device=device)
     kp = api.to_chunked(k, w.layout, w.n_chunks)
     vp = api.to_chunked(v, w.layout, w.n_chunks)
-    qp = api.to_chunked(q, w.layout, w.n_chunks) if w.q_chunks is None else q
+    if w.q_chunks is None:
+        qp = gather_chunked(w, q)
+        assert torch.equal(api.to_chunked(q, w.layout, w.n_chunks), qp)
+    else:
+        qp = q
     return qp, kp, vp, q, k, v
 
 

@@ -17,7 +17,7 @@ from oracle import attention as OA
 from oracle import backward as OB
 from oracle import layout as OL
 
-from .parity_utils import TOL, max_abs, query_rows_positions
+from .parity_utils import TOL, max_abs, physical_inputs, query_rows_positions
 
 pytestmark = pytest.mark.gpu
 
@@ -31,10 +31,7 @@ DEV = "cuda"
 
 
 def _setup(w, seed_do):
-    q, k, v = synthetic.draw(w, device=DEV)
-    kp = api.to_chunked(k, w.layout, w.n_chunks)
-    vp = api.to_chunked(v, w.layout, w.n_chunks)
-    qp = api.to_chunked(q, w.layout, w.n_chunks) if w.q_chunks is None else q
+    qp, kp, vp, _, k, v = physical_inputs(w, device=DEV)
     do = synthetic.normal_draw(qp.shape, seed_do, dtype=torch.bfloat16, device=DEV)
     return qp, kp, vp, k, v, do
 
@@ -96,6 +93,23 @@ def test_forward_then_backward(layout, causal):
     w = synthetic.Workload("t", 1, 8, 2, 2048, 4, 128, "bf16", causal, layout, seed=41)
     qp, kp, vp, k, v, do = _setup(w, seed_do=43)
     out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=layout, causal=causal)
+    dq, dk, dv = api.ring_backward(qp, kp, vp, out, do, lse, seq=w.seq, n_chunks=w.n_chunks, layout=layout,
+                                   causal=causal)
+    torch.cuda.synchronize()
+    _, _, rdq, rdk, rdv = _oracle(w, qp, k, v, do)
+    _check(w, (dq, dk, dv), (rdq, rdk, rdv))
+
+
+@pytest.mark.parametrize("layout,causal", [("zigzag", True), ("contiguous", False)])
+def test_forward_fp32_out_then_backward(layout, causal):
+    """An fp32 forward output feeding the backward (its D = rowsum(dO * O)
+    reads fp32 out; dout stays bf16 with the same element strides)."""
+    print(f"case fwd(fp32 out)+bwd {layout} causal={causal}", flush=True)
+    w = synthetic.Workload("t", 1, 8, 2, 1600, 4, 128, "bf16", causal, layout, seed=47)
+    qp, kp, vp, k, v, do = _setup(w, seed_do=49)
+    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=layout, causal=causal,
+                                out_dtype=torch.float32)
+    assert out.dtype == torch.float32 and out.stride() == do.stride()
     dq, dk, dv = api.ring_backward(qp, kp, vp, out, do, lse, seq=w.seq, n_chunks=w.n_chunks, layout=layout,
                                    causal=causal)
     torch.cuda.synchronize()

@@ -12,7 +12,7 @@ import synthetic
 from oracle import attention as OA
 from oracle import layout as OL
 
-from .parity_utils import TOL, max_abs, oracle_all_rows, physical_inputs
+from .parity_utils import TOL, gather_chunked, max_abs, oracle_all_rows, physical_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -176,7 +176,7 @@ def test_growing_scores_reference_updates(profile, causal):
     k = ((t / (0.5 * c * d))[None, None, :, None] + 0.05 * k.float()).to(torch.bfloat16)
     kp = api.to_chunked(k, w.layout, w.n_chunks)
     vp = api.to_chunked(v, w.layout, w.n_chunks)
-    qp = api.to_chunked(q, w.layout, w.n_chunks)
+    qp = gather_chunked(w, q)
     out, lse = _ring(w, qp, kp, vp, out_dtype=torch.float32)
     ref, ref_lse = oracle_all_rows(w, qp, k, v, causal)
     assert max_abs(out, ref) <= TOL["bf16"]
@@ -370,7 +370,8 @@ def test_strided_inputs_and_outputs(splits):
                         kv_splits=splits)
     nws = ra.ra_ring_workspace_bytes(desc)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
-    qp = api.to_chunked(q.contiguous(), "striped", N)
+    pos = torch.from_numpy(OL.all_positions("striped", S, N))
+    qp = q.index_select(2, pos.to(DEV)).contiguous()
     kp = api.to_chunked(k.contiguous(), "striped", N)
     vp = api.to_chunked(v.contiguous(), "striped", N)
     # physical inputs copied back into strided views of the same shape
@@ -378,7 +379,6 @@ def test_strided_inputs_and_outputs(splits):
     qs.copy_(qp), ks.copy_(kp), vs.copy_(vp)
     ra.ra_ring_fwd(desc, qs, ks, vs, out, lse, ws, nws)
     torch.cuda.synchronize()
-    pos = torch.from_numpy(OL.all_positions("striped", S, N))
     ref, ref_lse = OA.attention_reference(qp.cpu(), k.cpu(), v.cpu(), causal=True, q_pos=pos.numpy(),
                                           k_pos=np.arange(S))
     assert max_abs(out, ref) <= TOL["bf16"] and max_abs(lse, ref_lse) <= TOL["bf16"]

@@ -127,3 +127,37 @@ def test_skipped_step_leaves_state():
                       n_chunks=w.n_chunks, layout="contiguous", causal=True, q_chunk=i)
     torch.cuda.synchronize()
     assert torch.equal(st.m, m0) and torch.equal(st.l, l0) and torch.equal(st.o, o0)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_rows_that_see_no_key_keep_their_state(dtype, d):
+    """Striped causal, query chunk i: the step that brings KV chunk j > i is a
+    masked pair in which query row 0 sees no key (key row k is visible from
+    row p only when k <= p - 1).  That step must leave row 0's m, l and o
+    exactly as they were, and m of every row whose maximum does not grow."""
+    print(f"case ring step rows without keys {dtype} d={d}", flush=True)
+    w = synthetic.Workload("t", 1, 4, 2, 1024, 8, d, dtype, True, "striped", seed=21)
+    qp, kp, vp, *_ = physical_inputs(w)
+    L, i = w.chunk, 2
+    qi = _chunk_rows(w, qp, i)
+    st = api.state_init(qi, kp)
+    # steps 0 .. i bring KV chunks i .. 0 (none after the query chunk)
+    for t in range(i + 1):
+        j = (i - t) % w.n_chunks
+        api.ring_step(st, qi, kp[:, :, j * L:(j + 1) * L], vp[:, :, j * L:(j + 1) * L], step=t, seq=w.seq,
+                      n_chunks=w.n_chunks, layout=w.layout, causal=True, q_chunk=i)
+    torch.cuda.synchronize()
+    m0, l0, o0 = st.m.clone(), st.l.clone(), st.o.clone()
+    t = i + 1
+    j = (i - t) % w.n_chunks
+    assert j > i
+    api.ring_step(st, qi, kp[:, :, j * L:(j + 1) * L], vp[:, :, j * L:(j + 1) * L], step=t, seq=w.seq,
+                  n_chunks=w.n_chunks, layout=w.layout, causal=True, q_chunk=i)
+    torch.cuda.synchronize()
+    assert torch.equal(st.m[:, :, 0], m0[:, :, 0])
+    assert torch.equal(st.l[:, :, 0], l0[:, :, 0])
+    assert torch.equal(st.o[:, :, 0], o0[:, :, 0])
+    # rows whose running maximum did not move hand m back bit for bit
+    same = st.m == m0
+    assert same[:, :, 0].all()
+    assert (st.m >= m0).all()

@@ -116,9 +116,21 @@ def test_schedule_capacity_and_range_errors():
 # ---------------------------------------------------------------------------
 # Validation: every case below must fail before any HIP call (no GPU here).
 # Fake device pointers are aligned non-null integers; they are never used.
+# Where a GPU is present these tests are skipped: a regression in a check (or
+# in a no-launch early exit) would otherwise hand the made-up addresses to a
+# kernel.
 # ---------------------------------------------------------------------------
 
 P = 1 << 20  # fake aligned pointer
+
+
+def _gpu_present() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0   # counts devices without initialising HIP
+
+
+pytestmark = pytest.mark.skipif(_gpu_present(), reason="fake device pointers: host validation is checked "
+                                                       "where no GPU is present")
 
 
 def _adesc(**kw):
@@ -309,3 +321,27 @@ def test_ring_step_wholly_future_is_a_no_op():
     # and 2, wholly after it; the call returns OK without launching anything
     for t in (2, 3):
         assert _step(t, layout="contiguous", first=1, count=1) == ra.RA_OK
+
+
+def _bwd(r, **ptrs):
+    p = dict(q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, ws=P)
+    p.update(ptrs)
+    nws = ra.ra_ring_bwd_workspace_bytes(r)
+    return ra._lib.ra_ring_bwd(ctypes.byref(r), p["q"], p["k"], p["v"], p["out"], p["dout"], p["lse"], p["dq"],
+                               p["dk"], p["dv"], p["ws"], nws, None)
+
+
+def test_ring_bwd_validation():
+    r = _ring_desc()
+    assert ra.ra_ring_bwd_workspace_bytes(r) == 2 * 1 * 2 * 256 * 4
+    assert _bwd(_ring_desc(d=64, in_dtype=ra.RA_F32)) == ra.RA_ERR_UNSUPPORTED
+    assert _bwd(r, dout=None) == ra.RA_ERR_INVALID_ARG
+    assert _bwd(r, ws=None) == ra.RA_ERR_INVALID_ARG
+    assert _bwd(r, dq=P + 4) == ra.RA_ERR_INVALID_ARG
+    # dout is bf16 and shares the strides of out: an fp32 out whose row stride
+    # is 4 mod 8 elements would misalign its 16-byte pieces
+    r32 = _ring_desc(out_dtype=ra.RA_F32, out_s=132)
+    assert _bwd(r32) == ra.RA_ERR_INVALID_ARG
+    assert "multiples of 8" in ra.ra_last_error()
+    rs = _ring_desc()
+    assert ra._lib.ra_ring_bwd(ctypes.byref(rs), P, P, P, P, P, P, P, P, P, P, 8, None) == ra.RA_ERR_WORKSPACE

@@ -35,28 +35,30 @@ def _read_golden(name):
 # ---------------------------------------------------------------------------
 
 def test_glossary_four_device_simulation():
-    """The glossary page's four-device run, redone in fp32 as the page describes
-    it, prints True at atol 1e-5; the oracle must agree with it at that
-    tolerance and with the fp32 full softmax as well."""
+    """The glossary page's four-device experiment (Ultralytics glossary page
+    "Ring Attention", section "How Ring Attention works") on its own draw, in
+    fp32: device i holds query block i and, at step t, key/value block
+    (i - t) mod 4; it adds the unnormalized exponentials of its scaled scores
+    to a numerator and a denominator.  The page reports that the result
+    matches full softmax attention at atol 1e-5; the oracle must agree with
+    the simulated devices and with the fp32 full softmax at that tolerance."""
     g = _read_golden("glossary_four_device_simulation.txt")
     nd, blk, dim, atol = int(g["n_devices"]), int(g["block"]), int(g["dim"]), float(g["atol"])
     q, k, v = synthetic.tiny_sim_draw()
     assert q.shape == (nd * blk, dim)
-    qb, kb, vb = q.chunk(nd), k.chunk(nd), v.chunk(nd)
-    sim = []
-    for i in range(nd):
-        num = torch.zeros(blk, dim)
-        den = torch.zeros(blk, 1)
-        for step in range(nd):
-            j = (i - step) % nd
-            w = torch.exp(qb[i] @ kb[j].T / math.sqrt(dim))
-            num += w @ vb[j]
-            den += w.sum(dim=-1, keepdim=True)
-        sim.append(num / den)
-    sim = torch.cat(sim)
+    # which KV block each device holds at each step (the ring order), as one table
+    visit = (torch.arange(nd)[:, None] - torch.arange(nd)[None, :]) % nd          # [device, step]
+    q_dev = q.view(nd, blk, dim)                                                   # [device, row, dim]
+    k_held, v_held = k.view(nd, blk, dim)[visit], v.view(nd, blk, dim)[visit]    # [device, step, key, dim]
+    # every device's step-wise weights at once: 8 x 8 score blocks, unnormalized
+    w_steps = torch.exp(torch.einsum("irc,itkc->itrk", q_dev, k_held) / math.sqrt(dim))
+    numer = torch.einsum("itrk,itkc->irc", w_steps, v_held)                       # summed over steps
+    denom = w_steps.sum(dim=(1, 3)).unsqueeze(-1)
+    sim = (numer / denom).reshape(nd * blk, dim)
     full32 = torch.softmax(q @ k.T / math.sqrt(dim), dim=-1) @ v
     verdict = torch.allclose(sim, full32, atol=atol)
     assert str(verdict) == g["verdict"]
+    assert tuple(w_steps.shape[2:]) == tuple(int(x) for x in g["score_block"].split("x"))
 
     shp = (1, 1, nd * blk, dim)
     ref, lse = A.attention_reference(q.reshape(shp), k.reshape(shp), v.reshape(shp))
