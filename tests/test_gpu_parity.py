@@ -145,8 +145,10 @@ def test_sharp_scores_running_max():
     qp, kp, vp, q, k, v = physical_inputs(w)
     out, lse = _ring(w, qp, kp, vp, out_dtype=torch.float32)
     ref, ref_lse = oracle_all_rows(w, qp, k, v, False)
-    assert max_abs(out, ref) <= TOL["bf16"]
-    assert max_abs(lse, ref_lse) <= TOL["bf16"] * 10  # lse ~ 40: relative 5e-3
+    e_out, e_lse = max_abs(out, ref), max_abs(lse, ref_lse)
+    print(f"  max-abs out {e_out:.3e} lse {e_lse:.3e} (largest lse {np.abs(ref_lse).max():.1f})", flush=True)
+    assert e_out <= TOL["bf16"]
+    assert e_lse <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("profile", ["ramp_fast", "ramp_slow", "falling", "jumps"])
@@ -180,8 +182,9 @@ def test_growing_scores_reference_updates(profile, causal):
     out, lse = _ring(w, qp, kp, vp, out_dtype=torch.float32)
     ref, ref_lse = oracle_all_rows(w, qp, k, v, causal)
     assert max_abs(out, ref) <= TOL["bf16"]
-    # lse reaches about 200: relative 1e-4
-    assert max_abs(lse, ref_lse) <= 2e-4 * float(np.abs(np.asarray(ref_lse)).max()) + TOL["bf16"]
+    e_lse = max_abs(lse, ref_lse)
+    print(f"  max-abs lse {e_lse:.3e} (largest lse {np.abs(np.asarray(ref_lse)).max():.1f})", flush=True)
+    assert e_lse <= TOL["bf16"]
 
 
 # ---------------------------------------------------------------------------
