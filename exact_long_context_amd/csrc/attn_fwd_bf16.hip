@@ -234,10 +234,8 @@ struct RunCursor {
   }
 };
 
-// EXACT: chunk and step modes (the running state comes from and goes back to
-// HBM, relative to the exact running maximum, which is tracked beside the
-// reference); otherwise ring mode, which needs only the reference and
-// finalizes out / lse (or writes its split-KV partial).
+// EXACT: track the exact running maximum (chunk and step modes hand back the
+// state relative to it); ring mode needs only the reference.
 template <bool EXACT>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // four distinct arrays, so that the compiler can tell the buffer being
@@ -286,17 +284,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   // ---- running state (log2 units); l_run is this half-wave's partial sum
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
-  // chunk / step modes: the incoming m (natural) and its base-2 image; a row
-  // whose maximum does not move hands m back unchanged, not re-rounded
+  // chunk / step modes (EXACT): the incoming m (natural) and its base-2 image;
+  // a row whose maximum does not move hands m back unchanged, not re-rounded
   float m_in = -INFINITY, m_in2 = -INFINITY;
   f32x16 acc[4];  // acc[dvb]: O^T[dv = dvb*32 + 8(r/4) + 4g + r%4][query my_p]
 #pragma unroll
   for (int dvb = 0; dvb < 4; ++dvb) acc[dvb] = f32x16{};
-  if (EXACT && my_p < qg.len) {
+  if (a.mode != MODE_RING && my_p < qg.len) {
     const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + my_p;
-    m_in = a.m[mi];
-    m_ref = m_in == -INFINITY ? -INFINITY : m_in * LOG2E;
-    m_max = m_in2 = m_ref;
+    const float mv = a.m[mi];
+    m_ref = mv == -INFINITY ? -INFINITY : mv * LOG2E;
+    m_max = m_ref;
+    if constexpr (EXACT) {
+      m_in = mv;
+      m_in2 = m_ref;
+    }
     l_run = g == 0 ? a.l[mi] : 0.f;
     const float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + my_p) * a.o_ss;
 #pragma unroll
@@ -657,46 +659,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   // ---- epilogue
   float lt = sum_pair32(l_run);
   if (my_p >= qg.len) return;
-  if constexpr (!EXACT) {
-    if (a.kv_splits > 1) {
-      // partial of this KV range: normalized o and natural lse
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int64_t prow = (((int64_t)it.split * a.batch + it.b) * a.hq + h) * a.part_rows + qg.row_base + my_p;
-      float* orow = a.part_o + prow * D;
+  if (a.mode == MODE_RING && a.kv_splits > 1) {
+    // partial of this KV range: normalized o and natural lse
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t prow = (((int64_t)it.split * a.batch + it.b) * a.hq + h) * a.part_rows + qg.row_base + my_p;
+    float* orow = a.part_o + prow * D;
 #pragma unroll
-      for (int dvb = 0; dvb < 4; ++dvb)
+    for (int dvb = 0; dvb < 4; ++dvb)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 v4;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = acc[dvb][r4 * 4 + e] * inv;
-          *(f32x4*)(orow + dvb * 32 + r4 * 8 + 4 * g) = v4;
-        }
-      if (g == 0) a.part_lse[prow] = lt > 0.f ? (m_ref + __log2f(lt)) * LN2 : -INFINITY;
-    } else {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int64_t orow = (int64_t)it.b * a.out_sb + (int64_t)h * a.out_sh + (qg.row_base + my_p) * a.out_ss;
-#pragma unroll
-      for (int dvb = 0; dvb < 4; ++dvb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int dv = dvb * 32 + r4 * 8 + 4 * g;
-          f32x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = acc[dvb][r4 * 4 + e] * inv;
-          if (a.out_bf16) {
-            bf16x4 b4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) b4[e] = (__bf16)v4[e];
-            *(bf16x4*)((__bf16*)a.out + orow + dv) = b4;
-          } else {
-            *(f32x4*)((float*)a.out + orow + dv) = v4;
-          }
-        }
-      if (a.lse != nullptr && g == 0) {
-        const int64_t li = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + my_p;
-        a.lse[li] = lt > 0.f ? (m_ref + __log2f(lt)) * LN2 : -INFINITY;
+        for (int e = 0; e < 4; ++e) v4[e] = acc[dvb][r4 * 4 + e] * inv;
+        *(f32x4*)(orow + dvb * 32 + r4 * 8 + 4 * g) = v4;
       }
+    if (g == 0) a.part_lse[prow] = lt > 0.f ? (m_ref + __log2f(lt)) * LN2 : -INFINITY;
+  } else if (a.mode == MODE_RING) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t orow = (int64_t)it.b * a.out_sb + (int64_t)h * a.out_sh + (qg.row_base + my_p) * a.out_ss;
+#pragma unroll
+    for (int dvb = 0; dvb < 4; ++dvb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dv = dvb * 32 + r4 * 8 + 4 * g;
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[dvb][r4 * 4 + e] * inv;
+        if (a.out_bf16) {
+          bf16x4 b4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b4[e] = (__bf16)v4[e];
+          *(bf16x4*)((__bf16*)a.out + orow + dv) = b4;
+        } else {
+          *(f32x4*)((float*)a.out + orow + dv) = v4;
+        }
+      }
+    if (a.lse != nullptr && g == 0) {
+      const int64_t li = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + my_p;
+      a.lse[li] = lt > 0.f ? (m_ref + __log2f(lt)) * LN2 : -INFINITY;
     }
   } else {
     // chunk / step mode: hand back the state relative to the exact running maximum
@@ -704,7 +704,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     lt *= f;
     const int64_t mi = (int64_t)it.b * a.ml_sb + (int64_t)h * a.ml_sh + qg.row_base + my_p;
     if (g == 0) {
-      a.m[mi] = m_max == m_in2 ? m_in : m_max * LN2;
+      if constexpr (EXACT) a.m[mi] = m_max == m_in2 ? m_in : m_max * LN2;
+      else a.m[mi] = m_max == -INFINITY ? -INFINITY : m_max * LN2;
       a.l[mi] = lt;
     }
     float* orow = a.o + (int64_t)it.b * a.o_sb + (int64_t)h * a.o_sh + (qg.row_base + my_p) * a.o_ss;
