@@ -23,6 +23,7 @@
 // of their segment arrive as zeros.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fwd_common.h"
@@ -533,7 +534,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+// Workspace of the entry point that allocates nothing (ra_ring_bwd_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the GPU concerned.
+static __device__ __align__(256) unsigned char scratch[BWD_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
 }  // namespace
+
+hipError_t bwd_scratch(hipStream_t stream, void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // once per device, with that device current
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows_total = (int64_t)a.f.batch * a.f.hq * a.q_rows;

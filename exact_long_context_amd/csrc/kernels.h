@@ -96,6 +96,13 @@ hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
+// The backward's workspace without an allocation: the device address, on the
+// GPU that `stream` belongs to (the current GPU for the null stream), of a
+// file-scope array of BWD_SCRATCH_BYTES bytes (256-byte aligned).  Looked up
+// once per GPU; every call on that GPU shares the array.
+constexpr size_t BWD_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t bwd_scratch(hipStream_t stream, void** ptr);
+
 struct RowsArgs {  // [B, H, rows] fp32 tensors with strides (b, h), row stride 1; o-like with (b, h, s)
   int32_t batch, heads, rows, d;
   int64_t ml_sb, ml_sh;

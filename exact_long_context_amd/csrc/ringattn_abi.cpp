@@ -179,6 +179,68 @@ ra_status check_bwd_desc(const ra_ring_desc* desc) {
   return RA_OK;
 }
 
+// Validation and planning of the backward, everything but the workspace:
+// fills `a` (a.w left null) or returns the first rejection.
+ra_status plan_bwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, float* dq, float* dk, float* dv, ra::BwdArgs& a) {
+  ra_status st = check_bwd_desc(desc);
+  if (st != RA_OK) return st;
+  const ra_attn_desc* d = &desc->attn;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(RA_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk and dv must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(RA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t need = ra_ring_bwd_workspace_bytes(desc);
+  if (need > (size_t)I32_MAX) return fail(RA_ERR_UNSUPPORTED, "more than 2^28 query rows x heads per call");
+  const int64_t L = desc->seq / desc->n_chunks;
+  const int64_t q_rows = (int64_t)desc->q_chunk_count * L;
+  // query rows and dout rows of one head are addressed with 32-bit byte offsets
+  const int64_t qstride = (d->q.s > d->out.s ? d->q.s : d->out.s) * 2;
+  if ((q_rows - 1) * qstride + d->d * 2 > I32_MAX)
+    return fail(RA_ERR_UNSUPPORTED, "one head's query or dout rows span more than 2 GiB (rows x row stride)");
+  const int32_t nseg = ra::num_segments(desc->layout);
+  if ((st = check_kv_span(d, desc->seq, (int64_t)desc->n_chunks * nseg)) != RA_OK) return st;
+
+  std::memset(&a, 0, sizeof(a));
+  fill_common(a.f, d, q, k, v);
+  a.f.out = const_cast<void*>(out);
+  a.f.mode = ra::MODE_RING;
+  a.f.causal = desc->causal;
+  a.f.layout = desc->layout;
+  a.f.n_chunks = desc->n_chunks;
+  a.f.seq = desc->seq;
+  a.f.q_first = desc->q_chunk_first;
+  a.f.q_count = desc->q_chunk_count;
+  a.f.lq = (int32_t)L;
+  a.f.lk = (int32_t)L;
+  if ((st = plan_launch(a.f, true, L / nseg, nseg, desc->q_chunk_count)) != RA_OK) return st;
+  a.dout = dout;
+  a.lse_in = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.w = nullptr;
+  a.q_rows = (int32_t)q_rows;
+  a.scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->d));
+  const int64_t kv_tps = (L / nseg + 255) / 256;
+  const int64_t n_kv = (int64_t)d->batch * d->hkv * desc->n_chunks * nseg * kv_tps;
+  if (n_kv > I32_MAX) return fail(RA_ERR_INVALID_ARG, "problem too large for one launch");
+  a.kv_tiles_per_seg = (int32_t)kv_tps;
+  a.n_work_kv = (int32_t)n_kv;
+  return RA_OK;
+}
+
+// The three backward launches, in order, on one stream.
+ra_status launch_bwd(const ra::BwdArgs& a, hipStream_t s0, const char* who) {
+  char what[96];
+  ra_status st;
+  std::snprintf(what, sizeof(what), "%s (prep)", who);
+  if ((st = hip_status(ra::launch_bwd_prep(a, s0), what)) != RA_OK) return st;
+  std::snprintf(what, sizeof(what), "%s (dq)", who);
+  if ((st = hip_status(ra::launch_attn_bwd_dq_bf16(a, s0), what)) != RA_OK) return st;
+  std::snprintf(what, sizeof(what), "%s (dk, dv)", who);
+  return hip_status(ra::launch_attn_bwd_dkdv_bf16(a, s0), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,55 +467,34 @@ size_t ra_ring_bwd_workspace_bytes(const ra_ring_desc* desc) {
 ra_status ra_ring_bwd(const ra_ring_desc* desc, const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, float* dq, float* dk, float* dv, void* workspace,
                       size_t workspace_bytes, ra_stream stream) {
-  ra_status st = check_bwd_desc(desc);
+  ra::BwdArgs a;
+  ra_status st = plan_bwd(desc, q, k, v, out, dout, lse, dq, dk, dv, a);
   if (st != RA_OK) return st;
-  const ra_attn_desc* d = &desc->attn;
-  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
-    return fail(RA_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk, dv and workspace must be non-NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
-    return fail(RA_ERR_INVALID_ARG, "tensor pointers and the workspace must be 16-byte aligned");
+  if (workspace == nullptr || !aligned16(workspace))
+    return fail(RA_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
   const size_t need = ra_ring_bwd_workspace_bytes(desc);
   if (workspace_bytes < need) return fail(RA_ERR_WORKSPACE, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
-  if (need > (size_t)I32_MAX) return fail(RA_ERR_UNSUPPORTED, "more than 2^28 query rows x heads per call");
-  const int64_t L = desc->seq / desc->n_chunks;
-  const int64_t q_rows = (int64_t)desc->q_chunk_count * L;
-  // query rows and dout rows of one head are addressed with 32-bit byte offsets
-  const int64_t qstride = (d->q.s > d->out.s ? d->q.s : d->out.s) * 2;
-  if ((q_rows - 1) * qstride + d->d * 2 > I32_MAX)
-    return fail(RA_ERR_UNSUPPORTED, "one head's query or dout rows span more than 2 GiB (rows x row stride)");
-  const int32_t nseg = ra::num_segments(desc->layout);
-  if ((st = check_kv_span(d, desc->seq, (int64_t)desc->n_chunks * nseg)) != RA_OK) return st;
-
-  ra::BwdArgs a;
-  std::memset(&a, 0, sizeof(a));
-  fill_common(a.f, d, q, k, v);
-  a.f.out = const_cast<void*>(out);
-  a.f.mode = ra::MODE_RING;
-  a.f.causal = desc->causal;
-  a.f.layout = desc->layout;
-  a.f.n_chunks = desc->n_chunks;
-  a.f.seq = desc->seq;
-  a.f.q_first = desc->q_chunk_first;
-  a.f.q_count = desc->q_chunk_count;
-  a.f.lq = (int32_t)L;
-  a.f.lk = (int32_t)L;
-  if ((st = plan_launch(a.f, true, L / nseg, nseg, desc->q_chunk_count)) != RA_OK) return st;
-  a.dout = dout;
-  a.lse_in = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv;
   a.w = static_cast<float*>(workspace);
-  a.q_rows = (int32_t)q_rows;
-  a.scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->d));
-  const int64_t kv_tps = (L / nseg + 255) / 256;
-  const int64_t n_kv = (int64_t)d->batch * d->hkv * desc->n_chunks * nseg * kv_tps;
-  if (n_kv > I32_MAX) return fail(RA_ERR_INVALID_ARG, "problem too large for one launch");
-  a.kv_tiles_per_seg = (int32_t)kv_tps;
-  a.n_work_kv = (int32_t)n_kv;
-  hipStream_t s0 = (hipStream_t)stream;
-  if ((st = hip_status(ra::launch_bwd_prep(a, s0), "ra_ring_bwd (prep)")) != RA_OK) return st;
-  if ((st = hip_status(ra::launch_attn_bwd_dq_bf16(a, s0), "ra_ring_bwd (dq)")) != RA_OK) return st;
-  return hip_status(ra::launch_attn_bwd_dkdv_bf16(a, s0), "ra_ring_bwd (dk, dv)");
+  return launch_bwd(a, (hipStream_t)stream, "ra_ring_bwd");
+}
+
+ra_status ra_ring_bwd_noalloc(const ra_ring_desc* desc, const void* q, const void* k, const void* v,
+                              const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                              ra_stream stream) {
+  ra::BwdArgs a;
+  ra_status st = plan_bwd(desc, q, k, v, out, dout, lse, dq, dk, dv, a);
+  if (st != RA_OK) return st;
+  const size_t need = ra_ring_bwd_workspace_bytes(desc);
+  static_assert(ra::BWD_SCRATCH_BYTES == RA_BWD_NOALLOC_MAX_BYTES, "scratch size and header limit differ");
+  if (need > (size_t)RA_BWD_NOALLOC_MAX_BYTES)
+    return fail(RA_ERR_UNSUPPORTED, "ra_ring_bwd_noalloc: the call needs %zu workspace bytes, more than its %u "
+                "(at most %u batch x query heads x query rows); use ra_ring_bwd with a workspace",
+                need, (unsigned)RA_BWD_NOALLOC_MAX_BYTES, (unsigned)(RA_BWD_NOALLOC_MAX_BYTES / 8));
+  void* ws = nullptr;
+  if ((st = hip_status(ra::bwd_scratch((hipStream_t)stream, &ws), "ra_ring_bwd_noalloc (scratch lookup)")) != RA_OK)
+    return st;
+  a.w = static_cast<float*>(ws);
+  return launch_bwd(a, (hipStream_t)stream, "ra_ring_bwd_noalloc");
 }
 
 ra_status ra_layout_positions(int32_t layout, int64_t seq, int32_t n_chunks, int32_t chunk, int64_t* pos) {

@@ -29,6 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(5)
 RA_F32, RA_BF16 = 0, 1
 RA_MAX_KV_SPLITS = 64
+RA_BWD_NOALLOC_MAX_BYTES = 16 << 20
 RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
 RA_FULL, RA_MASKED, RA_SKIP = 0, 1, 2
 LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED, "zigzag": RA_LAYOUT_ZIGZAG}
@@ -84,6 +85,7 @@ _sigs = {
     "ra_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_P(ra_ring_desc)]),
     "ra_ring_bwd": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    ctypes.c_size_t, _vp]),
+    "ra_ring_bwd_noalloc": (ctypes.c_int, [_P(ra_ring_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ra_layout_positions": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            _P(ctypes.c_int64)]),
     "ra_ring_schedule": (ctypes.c_int, [_P(ra_ring_desc), ctypes.c_int32, _P(ra_task), ctypes.c_int32,
@@ -250,6 +252,11 @@ def ra_ring_bwd(desc: ra_ring_desc, q, k, v, out, dout, lse, dq, dk, dv, workspa
     _check(_lib.ra_ring_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, _stream(stream)),
            "ra_ring_bwd")
+
+
+def ra_ring_bwd_noalloc(desc: ra_ring_desc, q, k, v, out, dout, lse, dq, dk, dv, stream=None):
+    _check(_lib.ra_ring_bwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)), "ra_ring_bwd_noalloc")
 
 
 def ra_layout_positions(layout, seq: int, n_chunks: int, chunk: int) -> np.ndarray:

@@ -272,6 +272,28 @@ ra_status ra_ring_bwd(const ra_ring_desc* desc, const void* q, const void* k, co
                       const void* dout, const float* lse, float* dq, float* dk, float* dv, void* workspace,
                       size_t workspace_bytes, ra_stream stream);
 
+/* Largest workspace, in bytes, that ra_ring_bwd_noalloc brings with it: 8
+ * bytes per (batch, query head, query row) of the requested query chunks, so
+ * at most 2^21 such rows per call. */
+#define RA_BWD_NOALLOC_MAX_BYTES (16u << 20)
+
+/* ra_ring_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and results, without the workspace arguments.
+ * The workspace is a file-scope device array of RA_BWD_NOALLOC_MAX_BYTES in
+ * the library, one copy on each GPU it runs on, held until the process ends;
+ * it is looked up once per GPU (the GPU of `stream`, or the current GPU for
+ * the NULL stream) and nothing is allocated or freed by the call.  Every call
+ * on one GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams, other threads) race; serialize them.  Every workspace value a call
+ * reads is written earlier in the same call, so nothing needs clearing.
+ * A call that needs more than RA_BWD_NOALLOC_MAX_BYTES of workspace returns
+ * RA_ERR_UNSUPPORTED (use ra_ring_bwd with a workspace); a failed lookup
+ * returns RA_ERR_HIP. */
+ra_status ra_ring_bwd_noalloc(const ra_ring_desc* desc, const void* q, const void* k, const void* v,
+                              const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                              ra_stream stream);
+
 /* Host only.  pos[p] = global token position of row p of chunk `chunk`
  * (p = 0 .. seq/n_chunks - 1) under `layout`: the token split of the
  * "Context Parallelism" page (each GPU takes a chunk of consecutive tokens;

@@ -76,6 +76,16 @@ def test_backward_plans_three_launches():
     assert _calls() == n0 + 3 and LAST.value == 8 * 64 * 64
 
 
+def test_backward_without_allocation_plans_three_launches():
+    r = _desc("zigzag", 1 << 20, 32, 32, 8)
+    n0 = _calls()
+    assert ra._lib.ra_ring_bwd_noalloc(ctypes.byref(r), P, P, P, P, P, P, P, P, P, None) == ra.RA_OK
+    assert _calls() == n0 + 3 and LAST.value == 8 * 64 * 64
+    big = _desc("zigzag", 1 << 20, 32, 32, 8, count=3)   # 3 x 2^20 query rows x heads: 24 MiB
+    assert ra._lib.ra_ring_bwd_noalloc(ctypes.byref(big), P, P, P, P, P, P, P, P, P, None) == ra.RA_ERR_UNSUPPORTED
+    assert _calls() == n0 + 3
+
+
 def test_step_chunk_and_row_kernels():
     r = _desc("zigzag", 1 << 20, 32, 32, 8)
     n0 = _calls()

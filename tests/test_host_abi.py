@@ -345,3 +345,19 @@ def test_ring_bwd_validation():
     assert "multiples of 8" in ra.ra_last_error()
     rs = _ring_desc()
     assert ra._lib.ra_ring_bwd(ctypes.byref(rs), P, P, P, P, P, P, P, P, P, P, 8, None) == ra.RA_ERR_WORKSPACE
+
+
+def test_ring_bwd_noalloc_validation():
+    # the workspace it brings holds 2^21 (batch x query head x query row); beyond that it refuses
+    small = _ring_desc(S=1 << 16, N=4, count=4, hq=32, hkv=8)          # 32 x 65536 rows: 16 MiB, fits
+    assert ra.ra_ring_bwd_workspace_bytes(small) == ra.RA_BWD_NOALLOC_MAX_BYTES
+    big = _ring_desc(S=1 << 16, N=4, count=4, B=2, hq=32, hkv=8)       # twice that
+    assert ra._lib.ra_ring_bwd_noalloc(ctypes.byref(big), P, P, P, P, P, P, P, P, P, None) == \
+        ra.RA_ERR_UNSUPPORTED
+    assert "ra_ring_bwd_noalloc" in ra.ra_last_error()
+    assert ra._lib.ra_ring_bwd_noalloc(ctypes.byref(_ring_desc(d=64, in_dtype=ra.RA_F32)), P, P, P, P, P, P, P, P,
+                                       P, None) == ra.RA_ERR_UNSUPPORTED
+    assert ra._lib.ra_ring_bwd_noalloc(ctypes.byref(_ring_desc()), P, P, P, P, None, P, P, P, P, None) == \
+        ra.RA_ERR_INVALID_ARG
+    assert ra._lib.ra_ring_bwd_noalloc(ctypes.byref(_ring_desc(out_dtype=ra.RA_F32, out_s=132)), P, P, P, P, P, P,
+                                       P, P, P, None) == ra.RA_ERR_INVALID_ARG
