@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix and packed vector)
 KERNEL_SOURCE = os.path.join(ROOT, "exact_long_context_amd", "csrc", "attn_fwd_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_zigzag_1m_gqa.json")
 TRAFFIC_WORKLOAD = "zigzag_1m_gqa"   # the workload the counter runs were taken on
@@ -326,7 +327,7 @@ def balance_report(w, api, torch, reps=10):
 
 # Workloads the oracle leg checks: every element where the oracle finishes in
 # seconds to a minute, else sampled query rows (each against all its visible keys).
-ORACLE_FULL = ("tiny_sim", "mha_8k", "mha_8k_sharp", "causal_contig_32k")
+ORACLE_FULL = ("tiny_sim", "mha_8k", "mha_8k_sharp", "causal_contig_32k", "f32_causal_8k")
 ORACLE_SAMPLED = (("causal_striped_128k", 1024), ("zigzag_1m_gqa", 1024))
 
 
@@ -655,7 +656,7 @@ def main():
     if not args.no_others:
         # launches per workload: at least 50 for the small ones, 10 for the large ones
         for name, n in (("tiny_sim", 200), ("mha_8k", 50), ("mha_8k_sharp", 50), ("causal_contig_32k", 50),
-                        ("causal_striped_128k", 10), ("usp_1m_share", 10)):
+                        ("causal_striped_128k", 10), ("usp_1m_share", 10), ("f32_causal_8k", 20)):
             wo = synthetic.WORKLOADS[name]
             fo = workload_flop(wo, ra)
             t = launch_stats(time_workload(wo, max(n, args.steps), 3, api, torch))
@@ -663,6 +664,9 @@ def main():
                             "tflops_at_median": round(fo / (t["median"] * 1e-3) / 1e12, 4), "flop": fo}
             if wo.dtype == "bf16":
                 others[name]["computed_tile_flop"] = computed_tile_flop(wo, ra)
+            else:
+                # fp32 inputs run on the fp32 matrix cores (v_mfma_f32_32x32x2_f32)
+                others[name]["frac_of_fp32_mfma_peak"] = round(others[name]["tflops"] / PEAK_FP32_TFLOPS, 4)
             log(f"  {name}: {t['mean']:.4f} ms (median {t['median']:.4f}, min {t['min']:.4f})  "
                 f"{others[name]['tflops']} TFLOP/s")
             torch.cuda.empty_cache()

@@ -110,8 +110,8 @@ void fill_common(ra::FwdArgs& a, const ra_attn_desc* d, const void* q, const voi
 
 // Work decomposition.  bf16: 8 waves of 32 rows per workgroup; the waves are
 // query heads of one KV head when the group size allows (GQA shares every K/V
-// tile over the heads), else consecutive row blocks of one head.  fp32: one
-// wave of 64 rows.
+// tile over the heads), else consecutive row blocks of one head.  fp32: 4
+// waves of 32 rows of one head.
 ra_status plan_launch(ra::FwdArgs& a, bool bf16, int64_t seg_len, int32_t nseg_q, int32_t q_count) {
   const int32_t G = a.hq / a.hkv;
   if (bf16) {
@@ -119,8 +119,9 @@ ra_status plan_launch(ra::FwdArgs& a, bool bf16, int64_t seg_len, int32_t nseg_q
     a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
     a.rows_per_wg = 32 * 8 / a.heads_per_wg;
   } else {
+    // 4 waves of 32 rows of one head
     a.heads_per_wg = 1;
-    a.rows_per_wg = 64;
+    a.rows_per_wg = 128;
   }
   a.nseg_q = nseg_q;
   const int64_t tps = (seg_len + a.rows_per_wg - 1) / a.rows_per_wg;
@@ -445,11 +446,11 @@ ra_status ra_ring_kv_splits_hint(const ra_ring_desc* desc, int32_t* splits) {
   fill_common(a, d, nullptr, nullptr, nullptr);
   const int32_t nseg = ra::num_segments(desc->layout);
   if ((st = plan_launch(a, bf16, d->lq / nseg, nseg, desc->q_chunk_count)) != RA_OK) return st;
-  // Below two workgroups per compute unit (a bf16 workgroup fills one; the
-  // one-wave fp32 workgroups share one), split to about four, so that short
+  // Below two workgroups per compute unit (a bf16 workgroup fills one, an
+  // fp32 one of 4 waves about half of one), split to about four, so that short
   // ranges also even out query tiles of different causal work; never more
   // ranges than about one per four KV tiles of 64 keys of the sequence.
-  const int64_t enough = bf16 ? 512 : 2048;
+  const int64_t enough = bf16 ? 512 : 1024;
   int64_t s = a.n_work >= enough ? 1 : (2 * enough + a.n_work - 1) / a.n_work;
   const int64_t cap = desc->seq / 256 > 1 ? desc->seq / 256 : 1;
   if (s > cap) s = cap;

@@ -17,6 +17,8 @@ Workloads (all batch 1, i.i.d. N(0, 1) entries):
 * ``zigzag_1m_gqa``  -- 32 query heads sharing 8 KV heads, 1048576 tokens in
   32 zig-zag chunks of 32768; one query chunk is computed against all 32 KV
   chunks.
+* ``f32_causal_8k``  -- fp32 inputs at d = 128: 8 heads, 8192 tokens in 4
+  contiguous chunks, causal (the fp32 path at a real head dimension).
 * ``usp_1m_share``   -- the same layer as one GPU's share under the hybrid of
   the youngju.dev page (``hybrid_ulysses_ring_attention``) with a head
   all-to-all over 8 GPUs and a ring over 4: 4 query heads sharing 1 KV head,
@@ -73,6 +75,7 @@ WORKLOADS = {
     "causal_striped_128k": Workload("causal_striped_128k", 1, 8, 8, 131072, 16, 128, "bf16", True, "striped", 4),
     "zigzag_1m_gqa": Workload("zigzag_1m_gqa", 1, 32, 8, 1048576, 32, 128, "bf16", True, "zigzag", 5, q_chunks=(0,)),
     "usp_1m_share": Workload("usp_1m_share", 1, 4, 1, 1048576, 4, 128, "bf16", True, "zigzag", 6, q_chunks=(0,)),
+    "f32_causal_8k": Workload("f32_causal_8k", 1, 8, 8, 8192, 4, 128, "f32", True, "contiguous", 7),
 }
 
 
