@@ -29,7 +29,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix and packed vector)
-KERNEL_SOURCE = os.path.join(ROOT, "exact_long_context_amd", "csrc", "attn_fwd_bf16.hip")
+# the sources the forward kernel is compiled from (the traffic record is keyed by their hash)
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_long_context_amd", "csrc", f)
+                  for f in ("attn_fwd_bf16.hip", "fwd_common.h", "kernels.h", "schedule.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_zigzag_1m_gqa.json")
 TRAFFIC_WORKLOAD = "zigzag_1m_gqa"   # the workload the counter runs were taken on
 
@@ -517,14 +519,20 @@ def mfma_ceiling(random_operands, iters=160000):
             "frac_of_peak": round(tf.value / PEAK_BF16_TFLOPS, 4)}
 
 
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(workload):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on this workload and on the kernel source as it is now."""
     if workload != TRAFFIC_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    h = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if rec.get("kernel_sha256") != h:
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -557,7 +565,7 @@ def write_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes=1 << 
     wf = w_copy * kib / copy_bytes
     read_b = f_attn * kib / rf
     write_b = w_attn * kib / wf
-    rec = {"kernel_sha256": hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest(),
+    rec = {"kernel_sources_sha256": kernel_sources_sha256(),
            "hbm_bytes_per_launch": read_b + write_b,
            "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
            "fetch_size_kib_per_launch": f_attn, "write_size_kib_per_launch": w_attn,

@@ -315,15 +315,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  // work item: (b, kvh, KV chunk j, segment sb, key tile kt)
   const int32_t nseg = num_segments(f.layout);
   const int32_t L = f.lq;
-  int32_t w = blockIdx.x;
+  // work item: (b, kvh, KV chunk j, segment sb, key tile kt).  When the KV
+  // streams (batch x KV head) split evenly over the 8 XCDs, workgroup w lands
+  // on XCD w % 8 with the other workgroups of its stream: they all walk the
+  // same query and dO rows (the query heads of one KV head), so that XCD's L2
+  // serves their tiles and no other XCD fetches them.
+  const int32_t per_stream = f.n_chunks * nseg * a.kv_tiles_per_seg;
+  const int32_t n_streams = f.batch * f.hkv;
+  int32_t w, stream;
+  if (n_streams % 8 == 0) {
+    const int32_t u = (int32_t)blockIdx.x >> 3;
+    stream = ((int32_t)blockIdx.x & 7) + 8 * (u / per_stream);
+    w = u % per_stream;
+  } else {
+    stream = (int32_t)blockIdx.x / per_stream;
+    w = (int32_t)blockIdx.x % per_stream;
+  }
   const int32_t kt = w % a.kv_tiles_per_seg; w /= a.kv_tiles_per_seg;
   const int32_t sb = w % nseg; w /= nseg;
-  const int32_t j = w % f.n_chunks; w /= f.n_chunks;
-  const int32_t kvh = w % f.hkv;
-  const int32_t b = w / f.hkv;
+  const int32_t j = w;
+  const int32_t kvh = stream % f.hkv;
+  const int32_t b = stream / f.hkv;
   const Segment kseg = segment_l(f.layout, L, f.n_chunks, j, sb);
   const int64_t k_row0 = (int64_t)j * L + kseg.row0;  // buffer row of the segment's row 0
   const int32_t kv_len = kseg.len;

@@ -22,13 +22,26 @@ struct WorkItem {
 // position of the rows), and, when the KV streams split evenly over the 8
 // XCDs, workgroup w lands on XCD w % 8 together with the other workgroups of
 // the same KV stream, so that tiles walking the same keys share that XCD's L2.
+// With xcd_swizzle = S in {2, 4} the streams are taken S at a time over the
+// whole chip instead (XCD w % 8 serves stream w % S of the current group),
+// one group after another: the K / V of the streams in flight then stays
+// within the memory-side cache, where walking all streams at once would not.
 // The KV ranges of one query tile (split-KV) take consecutive ranks.
 __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a, int32_t w) {
   const int32_t G = a.hq / a.hkv;
   const int32_t hg_count = G / a.heads_per_wg;
   const int32_t n_streams = a.batch * a.hkv;
   int32_t r, stream, hg;
-  if (a.xcd_swizzle) {
+  if (a.xcd_swizzle > 1) {
+    const int32_t S = a.xcd_swizzle;
+    const int32_t per_s = a.n_work / n_streams;  // workgroups per stream
+    const int32_t grp = w / (S * per_s);
+    const int32_t rem = w - grp * S * per_s;
+    stream = S * grp + rem % S;
+    const int32_t v = rem / S;
+    r = v / hg_count;
+    hg = v - r * hg_count;
+  } else if (a.xcd_swizzle) {
     const int32_t x = w & 7, u = w >> 3;
     const int32_t per = (n_streams >> 3) * hg_count;
     r = u / per;
