@@ -12,6 +12,7 @@ extern "C" {
 // read by the stubbed-launch tests through ctypes
 int ra_hostcheck_launches = 0;     // launcher calls so far
 long long ra_hostcheck_last_work = -1;  // workgroups (or rows) of the last call
+int ra_hostcheck_last_xcd = -1;    // workgroup-to-XCD order of the last forward-kernel call
 
 const char* hipGetErrorString(hipError_t) { return "stubbed HIP runtime"; }
 }
@@ -25,8 +26,14 @@ hipError_t note(long long work) {
 }  // namespace
 
 namespace ra {
-hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t) { return note(a.n_work); }
-hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t) { return note(a.n_work); }
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t) {
+  ra_hostcheck_last_xcd = a.xcd_swizzle;
+  return note(a.n_work);
+}
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t) {
+  ra_hostcheck_last_xcd = a.xcd_swizzle;
+  return note(a.n_work);
+}
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t) { return note((long long)a.f.batch * a.f.hq * a.q_rows); }
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t) { return note(a.f.n_work); }
 hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, hipStream_t) { return note(a.n_work_kv); }

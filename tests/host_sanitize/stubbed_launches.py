@@ -15,6 +15,7 @@ ra = pytest.importorskip("exact_long_context_amd.ringattn")
 try:
     LAUNCHES = ctypes.c_int.in_dll(ra._lib, "ra_hostcheck_launches")
     LAST = ctypes.c_longlong.in_dll(ra._lib, "ra_hostcheck_last_work")
+    LAST_XCD = ctypes.c_int.in_dll(ra._lib, "ra_hostcheck_last_xcd")
 except ValueError:
     pytest.skip("needs the host-only build with stand-in launchers", allow_module_level=True)
 
@@ -43,18 +44,21 @@ def _calls():
     return LAUNCHES.value
 
 
-@pytest.mark.parametrize("name,args,work", [
-    ("zigzag_1m_gqa", ("zigzag", 1 << 20, 32, 32, 8), 4096),          # 8 streams x 2 segments x 256 tiles
-    ("causal_contig_32k", ("contiguous", 1 << 15, 8, 32, 32, 1, 0, 8), 4096),
-    ("causal_striped_128k", ("striped", 1 << 17, 16, 8, 8, 1, 0, 16), 4096),
-    ("mha_8k", ("contiguous", 8192, 4, 8, 8, 0, 0, 4), 256),
-    ("usp_1m_share", ("zigzag", 1 << 20, 4, 4, 1), 4096),        # 1 stream x 2 segments x 2048 tiles
+# workgroup-to-XCD order: 1 = one KV stream per XCD (8 streams or a multiple),
+# 2 = the streams two at a time over all XCDs (two streams' K and V fit in
+# 128 MiB, all of them do not), 0 = no XCD order (streams not a multiple of 8)
+@pytest.mark.parametrize("name,args,work,xcd", [
+    ("zigzag_1m_gqa", ("zigzag", 1 << 20, 32, 32, 8), 4096, 1),       # 8 streams x 2 segments x 256 tiles
+    ("causal_contig_32k", ("contiguous", 1 << 15, 8, 32, 32, 1, 0, 8), 4096, 1),
+    ("causal_striped_128k", ("striped", 1 << 17, 16, 8, 8, 1, 0, 16), 4096, 2),   # 8 streams of 64 MiB
+    ("mha_8k", ("contiguous", 8192, 4, 8, 8, 0, 0, 4), 256, 1),
+    ("usp_1m_share", ("zigzag", 1 << 20, 4, 4, 1), 4096, 0),        # 1 stream x 2 segments x 2048 tiles
 ])
-def test_ring_fwd_plans(name, args, work):
+def test_ring_fwd_plans(name, args, work, xcd):
     r = _desc(*args)
     n0 = _calls()
     assert ra._lib.ra_ring_fwd(ctypes.byref(r), P, P, P, P, P, None, 0, None) == ra.RA_OK
-    assert _calls() == n0 + 1 and LAST.value == work
+    assert _calls() == n0 + 1 and LAST.value == work and LAST_XCD.value == xcd
 
 
 def test_split_kv_plans_two_launches():
