@@ -455,7 +455,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   //   otherwise: the exponentials first, against the current reference.  A
   //     lane whose 32 values sum to at most 2^8 has every P^T value at most
   //     2^8, the same bound the lazy reference keeps; if any lane's sum is
-  //     larger (or not finite, or the reference is still -inf) the tile maximum
+  //     larger or not finite (as while the reference is still -inf) the tile maximum
   //     is taken, the reference moves to it wherever it grew, and the
   //     exponentials are recomputed.  The result is the same update with the
   //     maximum skipped on nearly every tile.
@@ -472,7 +472,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     } else {
       side(1);
       float part = exponentials(m_ref, side);
-      if (__any(!(part <= 256.f) || m_ref == -INFINITY)) {
+      // part is a sum of exponentials, so not negative: as an unsigned bit
+      // pattern it exceeds that of 2^8 exactly when it is larger than 2^8,
+      // infinite (as while the reference is still -inf) or NaN; one compare
+      // instead of two and the merge of their masks
+      if (__builtin_amdgcn_ballot_w64(__float_as_uint(part) > 0x43800000u) != 0) {
         const float mx = tile_max();
         move_reference(mx > m_ref, mx);
         part = exponentials(m_ref == -INFINITY ? 0.f : m_ref, nothing);
