@@ -64,13 +64,9 @@ __device__ __forceinline__ uint32_t tr_src(int blk, int lane, uint32_t rs) {
   return (uint32_t)(4 * blk + (lane >> 4)) * rs + (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) << 4);
 }
 
-__device__ __forceinline__ void dma(const void* base, uint32_t nrec, unsigned char* dst, uint32_t voff, uint32_t soff) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, (int)soff, 0, 0);
-}
-
-// The same load written out, for kernels that manage vmcnt themselves: the compiler does not track
-// it, so it inserts no waits of its own before LDS reads it cannot tell apart from the load's target.
+// One 16-byte-per-lane buffer load that writes LDS directly (lane l to byte 16 l of a 1 KiB block
+// at dst), written out: the compiler does not track it, so it inserts no waits of its own before
+// LDS reads it cannot tell apart from the load's target; the kernels wait for vmcnt themselves.
 // dst is a wave-uniform LDS byte address.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -144,13 +140,13 @@ constexpr int BNQ = 32;
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
-  // per buffer: K natural (S^T = K Q^T), K transposing (dQ^T += K^T dS^T), V natural (dP^T = V dO^T)
-  __shared__ __attribute__((aligned(1024))) unsigned char kn0[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char kn1[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char kt0[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char kt1[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char vn0[TILE32];
-  __shared__ __attribute__((aligned(1024))) unsigned char vn1[TILE32];
+  // Two buffers, each of K natural (S^T = K Q^T), K transposing (dQ^T += K^T dS^T) and V natural
+  // (dP^T = V dO^T), in one array: buffer B of tile kind T at (3 B + T) TILE32.  The loop body is one
+  // tile with the buffer index a loop variable (two unrolled bodies made the compiler copy the dQ
+  // accumulators between register sets on every tile); the loads are written out (dma_untracked)
+  // and waited for explicitly, so the compiler adds no waits for them before the operand reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[6 * TILE32];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -182,6 +178,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const int64_t rows_total = (int64_t)f.batch * f.hq * a.q_rows;
   const float w1c = row_ok ? a.w[wrow] * c2 : 0.f;            // -lse log2(e)
   const float negD = row_ok ? a.w[rows_total + wrow] : 0.f;   // -D
+  f32x16 negD16;  // the dP^T accumulator starts at -D (every register of a lane is its query row)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negD16[r] = negD;
 
   const unsigned char* Kg = (const unsigned char*)f.k + ((int64_t)it.b * f.k_sb + (int64_t)it.kvh * f.k_sh) * 2;
   const unsigned char* Vg = (const unsigned char*)f.v + ((int64_t)it.b * f.v_sb + (int64_t)it.kvh * f.v_sh) * 2;
@@ -201,22 +200,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 
   TileCursor<BNQ> cur = make_cursor<BNQ>(f, qg, wg_p_hi < wg_p0 ? -1 : wg_p_hi);
   if (wg_p_hi < wg_p0) cur.done = true;
-  auto stage = [&](const TileCursor<BNQ>& c, auto bc) __attribute__((always_inline)) {
-    constexpr int B = decltype(bc)::value;
+  auto stage = [&](const TileCursor<BNQ>& c, int B) __attribute__((always_inline)) {
     const uint32_t nk = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * kss + ROWB;
     const uint32_t nv = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * vss + ROWB;
     const uint32_t sk = (uint32_t)(c.kv_row + c.k0) * kss, sv = (uint32_t)(c.kv_row + c.k0) * vss;
-    dma(Kg, nk, (B ? kn1 : kn0) + blk_dst, kn_src, sk);
-    dma(Kg, nk, (B ? kt1 : kt0) + blk_dst, kt_src, sk);
-    dma(Vg, nv, (B ? vn1 : vn0) + blk_dst, vn_src, sv);
+    const uint32_t base = lds0 + (uint32_t)(3 * B * TILE32 + blk_dst);
+    dma_untracked(Kg, nk, base, kn_src, sk);
+    dma_untracked(Kg, nk, base + TILE32, kt_src, sk);
+    dma_untracked(Vg, nv, base + 2 * TILE32, vn_src, sv);
   };
 
-  auto compute = [&](const TileCursor<BNQ>& c, auto bc) __attribute__((always_inline)) {
-    constexpr int B = decltype(bc)::value;
-    const unsigned char* kn = B ? kn1 : kn0;
-    const unsigned char* kt = B ? kt1 : kt0;
-    const unsigned char* vn = B ? vn1 : vn0;
-    f32x16 s = {}, dp = {};
+  auto compute = [&](const TileCursor<BNQ>& c, int B) __attribute__((always_inline)) {
+    const unsigned char* kn = smem + 3 * B * TILE32;
+    const unsigned char* kt = kn + TILE32;
+    const unsigned char* vn = kn + 2 * TILE32;
+    f32x16 s = {}, dp = negD16;  // dp: dP^T - D
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       s = mfma(*(const bf16x8*)(kn + k_lane + 512 * ks), qf[ks], s);
@@ -241,7 +239,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, w1c));
-      dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] + negD));
+      dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -251,23 +249,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   };
 
   // double buffer: tile n in buffer n % 2; tile n + 1 is staged while tile n is computed
-  if (!cur.done) stage(cur, std::integral_constant<int, 0>{});
+  if (!cur.done) stage(cur, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  auto step = [&](auto bc) __attribute__((always_inline)) {
-    constexpr int B = decltype(bc)::value;
+  for (int B = 0; !cur.done; B ^= 1) {
     TileCursor<BNQ> nxt = cur;
     nxt.advance();
-    if (!nxt.done) stage(nxt, std::integral_constant<int, B ^ 1>{});
-    compute(cur, bc);
+    if (!nxt.done) stage(nxt, B ^ 1);
+    compute(cur, B);
     cur = nxt;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile n + 1 is in LDS
     __syncthreads();
-  };
-  while (!cur.done) {
-    step(std::integral_constant<int, 0>{});
-    if (cur.done) break;
-    step(std::integral_constant<int, 1>{});
   }
 
   if (!row_ok) return;
