@@ -193,7 +193,10 @@ def time_memory_kernels(w, torch, reps=10):
     nb = 2 * k.numel() * k.element_size()
     timed("ra_permute to chunk-major (K)", lambda: ra.ra_permute(w.layout, True, k, kc, w.n_chunks, stream), nb)
     timed("ra_permute to logical (K)", lambda: ra.ra_permute(w.layout, False, kc, k, w.n_chunks, stream), nb)
-    del k, kc
+    kv = k.view(B, w.seq, Hkv, d).transpose(1, 2)   # the same bytes read as a [B, S, H, d] buffer
+    timed("ra_permute_strided [B, S, H, d] to chunk-major (K)",
+          lambda: ra.ra_permute_strided(w.layout, True, kv, kc, w.n_chunks, stream), nb)
+    del k, kc, kv
     torch.cuda.empty_cache()
 
     q = torch.empty(B, Hq, rows, d, dtype=torch.bfloat16, device="cuda")

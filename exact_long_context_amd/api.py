@@ -10,18 +10,23 @@ from . import ringattn as ra
 
 
 def to_chunked(x: torch.Tensor, layout: str, n_chunks: int, stream=None) -> torch.Tensor:
-    """Logical token order [B, H, S, d] -> chunk-major physical order."""
-    x = x.contiguous()
-    out = torch.empty_like(x)
-    ra.ra_permute(layout, True, x, out, n_chunks, stream)
+    """Logical token order [B, H, S, d] -> chunk-major physical order (a new
+    contiguous tensor).  x may be a strided view, e.g. a [B, S, H, d] buffer
+    transposed to [B, H, S, d]; its last dimension must be contiguous."""
+    if x.stride(-1) != 1:
+        x = x.contiguous()
+    out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    ra.ra_permute_strided(layout, True, x, out, n_chunks, stream)
     return out
 
 
 def from_chunked(x: torch.Tensor, layout: str, n_chunks: int, stream=None) -> torch.Tensor:
-    """Chunk-major physical order -> logical token order."""
-    x = x.contiguous()
-    out = torch.empty_like(x)
-    ra.ra_permute(layout, False, x, out, n_chunks, stream)
+    """Chunk-major physical order -> logical token order (a new contiguous
+    tensor); x may be a strided view with a contiguous last dimension."""
+    if x.stride(-1) != 1:
+        x = x.contiguous()
+    out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    ra.ra_permute_strided(layout, False, x, out, n_chunks, stream)
     return out
 
 

@@ -146,24 +146,27 @@ __global__ __launch_bounds__(ROW_THREADS) void split_merge_kernel(RowsArgs g, in
 }
 
 // Permutation: physical row c*L + p  <->  logical row pos(c, p).  Each thread
-// moves one UNIT-byte piece.
+// moves one UNIT-byte piece; a workgroup covers consecutive pieces of one
+// (batch, head) so that reads and writes of a row stay together.
 template <typename UNIT>
-__global__ __launch_bounds__(256) void permute_kernel(int32_t layout, int32_t to_chunked, int64_t bh_count,
-                                                      int64_t seq, int32_t n, int64_t units_per_row,
-                                                      const UNIT* __restrict__ src, UNIT* __restrict__ dst) {
+__global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a, const UNIT* __restrict__ src,
+                                                      UNIT* __restrict__ dst) {
+  const int64_t per_bh = a.seq * a.units_per_row;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = bh_count * seq * units_per_row;
-  if (t >= total) return;
-  const int64_t row = t / units_per_row;
-  const int64_t u = t - row * units_per_row;
-  const int64_t bh = row / seq;
-  const int64_t phys = row - bh * seq;
-  const int64_t L = seq / n;
+  if (t >= per_bh) return;
+  const int64_t phys = t / a.units_per_row;
+  const int64_t u = t - phys * a.units_per_row;
+  const int64_t L = a.seq / a.n_chunks;
   const int32_t c = (int32_t)(phys / L);
-  const int64_t logical = position(layout, seq, n, c, phys - (int64_t)c * L);
-  const int64_t base = bh * seq;
-  if (to_chunked) dst[(base + phys) * units_per_row + u] = src[(base + logical) * units_per_row + u];
-  else dst[(base + logical) * units_per_row + u] = src[(base + phys) * units_per_row + u];
+  const int64_t logical = position(a.layout, a.seq, a.n_chunks, c, phys - (int64_t)c * L);
+  const int64_t src_row = a.to_chunked ? logical : phys;
+  const int64_t dst_row = a.to_chunked ? phys : logical;
+  // (batch, head) pairs: grid rows, strided when there are more than the grid has
+  for (int64_t bh = blockIdx.y; bh < a.batch * a.heads; bh += gridDim.y) {
+    const int64_t b = bh / a.heads, h = bh - b * a.heads;
+    dst[b * a.dst_sb + h * a.dst_sh + dst_row * a.dst_ss + u] =
+        src[b * a.src_sb + h * a.src_sh + src_row * a.src_ss + u];
+  }
 }
 
 inline unsigned blocks_for(int64_t threads, int per) { return (unsigned)((threads + per - 1) / per); }
@@ -205,32 +208,26 @@ hipError_t launch_split_merge(const RowsArgs& g, int32_t kv_splits, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_permute(int32_t layout, int32_t to_chunked, int64_t batch_heads, int64_t seq, int32_t n_chunks,
-                          int64_t row_bytes, int unit, const void* src, void* dst, hipStream_t stream) {
-  const int64_t upr = row_bytes / unit;
-  const int64_t threads = batch_heads * seq * upr;
-  if (threads == 0) return hipSuccess;
-  const dim3 grid(blocks_for(threads, 256)), block(256);
+hipError_t launch_permute(const PermuteArgs& p, int unit, const void* src, void* dst, hipStream_t stream) {
+  const int64_t per_bh = p.seq * p.units_per_row;
+  const int64_t bh = p.batch * p.heads;
+  if (per_bh == 0 || bh == 0) return hipSuccess;
+  const dim3 grid(blocks_for(per_bh, 256), (unsigned)(bh < 65535 ? bh : 65535)), block(256);
   switch (unit) {
     case 16:
-      hipLaunchKernelGGL(permute_kernel<uint4>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
-                         n_chunks, upr, (const uint4*)src, (uint4*)dst);
+      hipLaunchKernelGGL(permute_kernel<uint4>, grid, block, 0, stream, p, (const uint4*)src, (uint4*)dst);
       break;
     case 8:
-      hipLaunchKernelGGL(permute_kernel<uint2>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
-                         n_chunks, upr, (const uint2*)src, (uint2*)dst);
+      hipLaunchKernelGGL(permute_kernel<uint2>, grid, block, 0, stream, p, (const uint2*)src, (uint2*)dst);
       break;
     case 4:
-      hipLaunchKernelGGL(permute_kernel<uint32_t>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
-                         n_chunks, upr, (const uint32_t*)src, (uint32_t*)dst);
+      hipLaunchKernelGGL(permute_kernel<uint32_t>, grid, block, 0, stream, p, (const uint32_t*)src, (uint32_t*)dst);
       break;
     case 2:
-      hipLaunchKernelGGL(permute_kernel<uint16_t>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
-                         n_chunks, upr, (const uint16_t*)src, (uint16_t*)dst);
+      hipLaunchKernelGGL(permute_kernel<uint16_t>, grid, block, 0, stream, p, (const uint16_t*)src, (uint16_t*)dst);
       break;
     default:
-      hipLaunchKernelGGL(permute_kernel<uint8_t>, grid, block, 0, stream, layout, to_chunked, batch_heads, seq,
-                         n_chunks, upr, (const uint8_t*)src, (uint8_t*)dst);
+      hipLaunchKernelGGL(permute_kernel<uint8_t>, grid, block, 0, stream, p, (const uint8_t*)src, (uint8_t*)dst);
       break;
   }
   return hipGetLastError();

@@ -121,7 +121,14 @@ hipError_t launch_merge(const RowsArgs& g, const float* lse_a, const float* o_a,
 // lse = -inf.  g gives the out / lse strides (ml_*, out_*); lse may be null.
 hipError_t launch_split_merge(const RowsArgs& g, int32_t kv_splits, const float* part_lse, const float* part_o,
                               void* out, int32_t out_bf16, float* lse, hipStream_t stream);
-hipError_t launch_permute(int32_t layout, int32_t to_chunked, int64_t batch_heads, int64_t seq, int32_t n_chunks,
-                          int64_t row_bytes, int unit, const void* src, void* dst, hipStream_t stream);
+// Row permutation between logical and chunk-major order.  Strides are in
+// `unit`-byte pieces ([batch, head, row] of src, then of dst); a row is
+// row_bytes / unit pieces, contiguous.
+struct PermuteArgs {
+  int32_t layout, to_chunked, n_chunks;
+  int64_t batch, heads, seq, units_per_row;
+  int64_t src_sb, src_sh, src_ss, dst_sb, dst_sh, dst_ss;
+};
+hipError_t launch_permute(const PermuteArgs& p, int unit, const void* src, void* dst, hipStream_t stream);
 
 }  // namespace ra

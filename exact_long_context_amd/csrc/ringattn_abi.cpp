@@ -562,8 +562,10 @@ ra_status ra_ring_schedule(const ra_ring_desc* desc, int32_t q_chunk, ra_task* t
   return RA_OK;
 }
 
-ra_status ra_permute(int32_t layout, int32_t to_chunked, int64_t batch, int64_t heads, int64_t seq,
-                     int32_t n_chunks, int64_t d, int32_t dtype, const void* src, void* dst, ra_stream stream) {
+ra_status ra_permute_strided(int32_t layout, int32_t to_chunked, int64_t batch, int64_t heads, int64_t seq,
+                             int32_t n_chunks, int64_t d, int32_t dtype, const void* src, int64_t src_sb,
+                             int64_t src_sh, int64_t src_ss, void* dst, int64_t dst_sb, int64_t dst_sh,
+                             int64_t dst_ss, ra_stream stream) {
   if (!src || !dst) return fail(RA_ERR_INVALID_ARG, "src and dst must be non-NULL");
   if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED && layout != RA_LAYOUT_ZIGZAG)
     return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
@@ -573,15 +575,41 @@ ra_status ra_permute(int32_t layout, int32_t to_chunked, int64_t batch, int64_t 
   if (layout == RA_LAYOUT_ZIGZAG && ((seq / n_chunks) % 2))
     return fail(RA_ERR_INVALID_ARG, "zig-zag needs an even chunk length");
   if (to_chunked != 0 && to_chunked != 1) return fail(RA_ERR_INVALID_ARG, "to_chunked must be 0 or 1");
-  const int64_t row_bytes = d * elem_bytes(dtype);
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
-  if (addr % elem_bytes(dtype)) return fail(RA_ERR_INVALID_ARG, "misaligned pointer");
-  // widest piece (16, 8, 4 or 2 bytes) that divides the row and both pointers
+  const int64_t strides[6] = {src_sb, src_sh, src_ss, dst_sb, dst_sh, dst_ss};
+  for (int64_t st : strides)
+    if (st < 0) return fail(RA_ERR_INVALID_ARG, "strides must not be negative");
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t row_bytes = d * eb;
+  // every piece a thread moves must be a whole number of elements inside one row: the widest of 16,
+  // 8, 4, 2 bytes that divides the row, both pointers and every stride in bytes
+  uint64_t bits = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | (uint64_t)row_bytes;
+  for (int64_t st : strides) bits |= (uint64_t)(st * eb);
+  if (bits % eb) return fail(RA_ERR_INVALID_ARG, "misaligned pointer");
   int unit = 16;
-  while ((row_bytes % unit) || (addr % unit)) unit >>= 1;
-  return hip_status(ra::launch_permute(layout, to_chunked, batch * heads, seq, n_chunks, row_bytes, unit, src, dst,
-                                       (hipStream_t)stream),
-                    "ra_permute");
+  while (bits % unit) unit >>= 1;
+  ra::PermuteArgs p;
+  p.layout = layout;
+  p.to_chunked = to_chunked;
+  p.n_chunks = n_chunks;
+  p.batch = batch;
+  p.heads = heads;
+  p.seq = seq;
+  p.units_per_row = row_bytes / unit;
+  p.src_sb = src_sb * eb / unit;
+  p.src_sh = src_sh * eb / unit;
+  p.src_ss = src_ss * eb / unit;
+  p.dst_sb = dst_sb * eb / unit;
+  p.dst_sh = dst_sh * eb / unit;
+  p.dst_ss = dst_ss * eb / unit;
+  return hip_status(ra::launch_permute(p, unit, src, dst, (hipStream_t)stream), "ra_permute");
+}
+
+ra_status ra_permute(int32_t layout, int32_t to_chunked, int64_t batch, int64_t heads, int64_t seq,
+                     int32_t n_chunks, int64_t d, int32_t dtype, const void* src, void* dst, ra_stream stream) {
+  // contiguous [batch, heads, seq, d]; the strides overflow only for shapes no buffer can hold
+  if (batch < 1 || heads < 1 || d < 1 || seq < 1) return fail(RA_ERR_INVALID_ARG, "bad shape");
+  return ra_permute_strided(layout, to_chunked, batch, heads, seq, n_chunks, d, dtype, src, heads * seq * d,
+                            seq * d, d, dst, heads * seq * d, seq * d, d, stream);
 }
 
 }  // extern "C"

@@ -92,6 +92,10 @@ _sigs = {
                                         _P(ctypes.c_int32)]),
     "ra_permute": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
+    "ra_permute_strided": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                          _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp]),
 }
 for _name, (_res, _args) in _sigs.items():
     _fn = getattr(_lib, _name)
@@ -285,3 +289,18 @@ def ra_permute(layout, to_chunked: bool, src, dst, n_chunks: int, stream=None):
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     _check(_lib.ra_permute(lay, 1 if to_chunked else 0, B, H, S, n_chunks, d, _dtype_code(src), _ptr(src),
                            _ptr(dst), _stream(stream)), "ra_permute")
+
+
+def ra_permute_strided(layout, to_chunked: bool, src, dst, n_chunks: int, stream=None):
+    """src, dst: [B, H, S, d] tensors (views allowed; last dimension contiguous)
+    of the same shape and dtype; element strides are passed as they are."""
+    if src.shape != dst.shape or src.dtype != dst.dtype:
+        raise ValueError("src and dst must have the same shape and dtype")
+    if src.dim() != 4 or src.stride(3) != 1 or dst.stride(3) != 1:
+        raise ValueError("[B, H, S, d] tensors with a contiguous last dimension expected")
+    B, H, S, d = src.shape
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    _check(_lib.ra_permute_strided(lay, 1 if to_chunked else 0, B, H, S, n_chunks, d, _dtype_code(src),
+                                   _ptr(src), src.stride(0), src.stride(1), src.stride(2),
+                                   _ptr(dst), dst.stride(0), dst.stride(1), dst.stride(2), _stream(stream)),
+           "ra_permute_strided")

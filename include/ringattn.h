@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 2
+#define RA_ABI_VERSION 3
 
 /* Largest ra_ring_desc.kv_splits. */
 #define RA_MAX_KV_SPLITS 64
@@ -328,6 +328,19 @@ ra_status ra_ring_schedule(const ra_ring_desc* desc, int32_t q_chunk, ra_task* t
 ra_status ra_permute(int32_t layout, int32_t to_chunked, int64_t batch, int64_t heads, int64_t seq,
                      int32_t n_chunks, int64_t d, int32_t dtype, const void* src, void* dst,
                      ra_stream stream);
+
+/* ra_permute on strided tensors: src and dst are [batch, heads, seq, d] of
+ * `dtype` with element strides (sb, sh, ss) each and a contiguous last
+ * dimension, so a [batch, seq, heads, d] buffer (the layout of the JAX ring
+ * listing on the youngju.dev page) is read or written in place of a
+ * transposed copy.  Strides must not be negative and pointers must be
+ * aligned to the element (else RA_ERR_INVALID_ARG).  The rows src reads and
+ * the rows dst writes must not overlap (not checked).  Same row maps and
+ * bit-exact copy as ra_permute. */
+ra_status ra_permute_strided(int32_t layout, int32_t to_chunked, int64_t batch, int64_t heads, int64_t seq,
+                             int32_t n_chunks, int64_t d, int32_t dtype, const void* src, int64_t src_sb,
+                             int64_t src_sh, int64_t src_ss, void* dst, int64_t dst_sb, int64_t dst_sh,
+                             int64_t dst_ss, ra_stream stream);
 
 #ifdef __cplusplus
 }

@@ -56,8 +56,7 @@ hipError_t bwd_scratch(hipStream_t, void** ptr) {
   *ptr = reinterpret_cast<void*>(uintptr_t(1) << 30);  // made up, never dereferenced
   return hipSuccess;
 }
-hipError_t launch_permute(int32_t, int32_t, int64_t batch_heads, int64_t seq, int32_t, int64_t, int, const void*,
-                          void*, hipStream_t) {
-  return note(batch_heads * seq);
+hipError_t launch_permute(const PermuteArgs& p, int, const void*, void*, hipStream_t) {
+  return note(p.batch * p.heads * p.seq);
 }
 }  // namespace ra

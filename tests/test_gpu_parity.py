@@ -73,6 +73,52 @@ def test_permute_round_trip_bit_exact(layout, S, N, dtype, d):
     assert torch.equal(z, x)
 
 
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+@pytest.mark.parametrize("layout,S,N", [("contiguous", 96, 8), ("striped", 96, 8), ("zigzag", 96, 8),
+                                        ("zigzag", 64, 32)])
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 16), (torch.bfloat16, 3),
+                                     (torch.float32, 5)])
+def test_permute_strided_bshd_bit_exact(layout, S, N, dtype, d):
+    """[B, S, H, d] buffers read and written in place through strided views,
+    against the oracle's positions; a destination with padded rows keeps its
+    padding."""
+    print(f"case permute strided {layout} {S} {N} {dtype} {d}", flush=True)
+    B, H = 2, 3
+    x_bshd = synthetic.normal_draw((B, S, H, d), seed=7 * S + d, dtype=dtype, device=DEV)
+    x = x_bshd.transpose(1, 2)                       # [B, H, S, d] view, row stride H d
+    phys = torch.from_numpy(OL.all_positions(layout, S, N)).to(DEV)
+    expect = x[:, :, phys].contiguous()
+    y = api.to_chunked(x, layout, N)                 # strided source, contiguous result
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y), _bits(expect))
+    # padded destination rows: [B, H, S, d + 5] buffer, the first d columns written
+    pad = torch.full((B, H, S, d + 5), -7.0, dtype=dtype, device=DEV)
+    ra.ra_permute_strided(layout, True, x, pad[..., :d], N)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(pad[..., :d].contiguous()), _bits(expect))
+    assert bool((pad[..., d:] == -7.0).all())
+    # back to logical order straight into a [B, S, H, d] buffer
+    z_bshd = torch.empty_like(x_bshd)
+    ra.ra_permute_strided(layout, False, y, z_bshd.transpose(1, 2), N)
+    back = api.from_chunked(pad[..., :d], layout, N)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(z_bshd), _bits(x_bshd))
+    assert torch.equal(_bits(back), _bits(x.contiguous()))
+
+
+def test_permute_many_heads_bit_exact():
+    """More (batch, head) pairs than one grid dimension holds (65535)."""
+    print("case permute 70000 heads", flush=True)
+    x = synthetic.normal_draw((1, 70000, 4, 2), seed=3, dtype=torch.bfloat16, device=DEV)
+    phys = torch.from_numpy(OL.all_positions("striped", 4, 2)).to(DEV)
+    y = api.to_chunked(x, "striped", 2)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y), _bits(x[:, :, phys].contiguous()))
+
+
 # ---------------------------------------------------------------------------
 # the fused ring on small and ragged shapes, every row compared
 # ---------------------------------------------------------------------------

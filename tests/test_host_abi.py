@@ -42,7 +42,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(ra.ra_attn_desc) == 6 * 8 + 2 * 4 + 6 * 24 + 4 + 4
     assert ctypes.sizeof(ra.ra_ring_desc) == ctypes.sizeof(ra.ra_attn_desc) + 8 + 6 * 4
     assert ctypes.sizeof(ra.ra_task) == 6 * 4 + 8 + 2 * 4
-    assert ra.ra_abi_version() == 2
+    assert ra.ra_abi_version() == 3
     assert ra.ra_status_str(0) == "ok" and ra.ra_status_str(3) == "workspace too small"
 
 
@@ -268,6 +268,20 @@ def test_permute_and_positions_validation():
     assert f(0, 1, 1, 1, 16, 4, 8, 4, P, P, None) == ra.RA_ERR_INVALID_ARG            # dtype
     assert f(0, 1, 1, 1, 16, 4, 8, ra.RA_F32, P + 2, P, None) == ra.RA_ERR_INVALID_ARG  # alignment
     assert f(0, 1, 1, 1, 16, 4, 8, ra.RA_F32, None, P, None) == ra.RA_ERR_INVALID_ARG
+    g = ra._lib.ra_permute_strided
+    ok = (0, 1, 2, 3, 16, 4, 8, ra.RA_F32, P, 3 * 16 * 8, 16 * 8, 8, P, 3 * 16 * 8, 16 * 8, 8, None)
+
+    def with_(**kw):
+        names = ["layout", "dir", "B", "H", "S", "N", "d", "dtype", "src", "ssb", "ssh", "sss",
+                 "dst", "dsb", "dsh", "dss", "stream"]
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return g(*a)
+    for bad in (dict(sss=-8), dict(dsh=-1), dict(ssb=-128), dict(src=None), dict(dst=None),
+                dict(src=P + 2), dict(dst=P + 6), dict(S=10, N=3), dict(layout=7), dict(dir=2),
+                dict(dtype=9), dict(B=0), dict(d=0), dict(layout=2, S=12, N=4)):
+        assert with_(**bad) == ra.RA_ERR_INVALID_ARG, bad
     with pytest.raises(ra.RingAttnError):
         ra.ra_layout_positions("zigzag", 12, 4, 0)
     with pytest.raises(ra.RingAttnError):
