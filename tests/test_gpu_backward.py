@@ -146,3 +146,18 @@ def test_backward_invariants_and_rejections():
     desc = ra.ring_desc(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=True, out=out, lse=lse)
     with pytest.raises(ra.RingAttnError):
         ra.ra_ring_bwd(desc, qp, kp, vp, out, do, lse, dq, dk, dv, ws, 8)
+
+
+def test_backward_is_deterministic():
+    """No atomics anywhere in the backward: two calls on the same inputs give
+    the same bits, also with a query-chunk subset and grouped heads."""
+    print("case bwd determinism", flush=True)
+    w = synthetic.Workload("t", 1, 8, 2, 2048, 8, 128, "bf16", True, "zigzag", seed=61, q_chunks=(2, 3, 4))
+    qp, kp, vp, k, v, do = _setup(w, seed_do=63)
+    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=True,
+                                q_chunk_first=2)
+    runs = [api.ring_backward(qp, kp, vp, out, do, lse, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout,
+                              causal=True, q_chunk_first=2) for _ in range(2)]
+    torch.cuda.synchronize()
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
