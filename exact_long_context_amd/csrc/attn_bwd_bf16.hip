@@ -132,19 +132,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: per query tile, the KV tiles of 32 keys in ring order
+// dQ: per query tile, the KV tiles of 64 keys in ring order
 // ---------------------------------------------------------------------------
 
-constexpr int BNQ = 32;
+constexpr int BNQ = 64;              // keys per tile
+constexpr int NHALF = BNQ / 32;      // 32-key MFMA blocks per tile
+constexpr int QTILE = BNQ * ROWB;    // bytes of one tile kind
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
   // Two buffers, each of K natural (S^T = K Q^T), K transposing (dQ^T += K^T dS^T) and V natural
-  // (dP^T = V dO^T), in one array: buffer B of tile kind T at (3 B + T) TILE32.  The loop body is one
+  // (dP^T = V dO^T), in one array: buffer B of tile kind T at (3 B + T) QTILE.  The loop body is one
   // tile with the buffer index a loop variable (two unrolled bodies made the compiler copy the dQ
   // accumulators between register sets on every tile); the loads are written out (dma_untracked)
   // and waited for explicitly, so the compiler adds no waits for them before the operand reads.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[6 * TILE32];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[6 * QTILE];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -184,8 +186,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const unsigned char* Kg = (const unsigned char*)f.k + ((int64_t)it.b * f.k_sb + (int64_t)it.kvh * f.k_sh) * 2;
   const unsigned char* Vg = (const unsigned char*)f.v + ((int64_t)it.b * f.v_sb + (int64_t)it.kvh * f.v_sh) * 2;
   const uint32_t kss = (uint32_t)(f.k_ss * 2), vss = (uint32_t)(f.v_ss * 2);
-  // DMA: wave w moves block w of each of the three tiles
-  const uint32_t kn_src = nat_src(wave, lane, kss), kt_src = tr_src(wave, lane, kss), vn_src = nat_src(wave, lane, vss);
+  // DMA: wave w moves blocks w + 8 i (i < NHALF) of each of the three tiles
+  uint32_t kn_src[NHALF], kt_src[NHALF], vn_src[NHALF];
+#pragma unroll
+  for (int i = 0; i < NHALF; ++i) {
+    kn_src[i] = nat_src(wave + 8 * i, lane, kss);
+    kt_src[i] = tr_src(wave + 8 * i, lane, kss);
+    vn_src[i] = nat_src(wave + 8 * i, lane, vss);
+  }
   const int blk_dst = __builtin_amdgcn_readfirstlane(wave * 1024);
 
   const int k_lane = k_pos(kperm(l32), g);  // natural operand, 16-d step ks: + 512 ks
@@ -203,23 +211,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     const uint32_t nk = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * kss + ROWB;
     const uint32_t nv = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * vss + ROWB;
     const uint32_t sk = (uint32_t)(c.kv_row + c.k0) * kss, sv = (uint32_t)(c.kv_row + c.k0) * vss;
-    const uint32_t base = lds0 + (uint32_t)(3 * B * TILE32 + blk_dst);
-    dma_untracked(Kg, nk, base, kn_src, sk);
-    dma_untracked(Kg, nk, base + TILE32, kt_src, sk);
-    dma_untracked(Vg, nv, base + 2 * TILE32, vn_src, sv);
+    const uint32_t base = lds0 + (uint32_t)(3 * B * QTILE + blk_dst);
+#pragma unroll
+    for (int i = 0; i < NHALF; ++i) {
+      dma_untracked(Kg, nk, base + 8192 * i, kn_src[i], sk);
+      dma_untracked(Kg, nk, base + QTILE + 8192 * i, kt_src[i], sk);
+      dma_untracked(Vg, nv, base + 2 * QTILE + 8192 * i, vn_src[i], sv);
+    }
   };
 
   auto compute = [&](const TileCursor<BNQ>& c, int B) __attribute__((always_inline)) {
-    const unsigned char* kn = smem + 3 * B * TILE32;
-    const unsigned char* kt = kn + TILE32;
-    const unsigned char* vn = kn + 2 * TILE32;
-    f32x16 s = {}, dp = negD16;  // dp: dP^T - D
+    const unsigned char* kn = smem + 3 * B * QTILE;
+    const unsigned char* kt = kn + QTILE;
+    const unsigned char* vn = kn + 2 * QTILE;
+    f32x16 s[NHALF], dp[NHALF];  // block hf: tile keys 32 hf ..; dp: dP^T - D
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      s = mfma(*(const bf16x8*)(kn + k_lane + 512 * ks), qf[ks], s);
-      dp = mfma(*(const bf16x8*)(vn + k_lane + 512 * ks), dof[ks], dp);
+    for (int hf = 0; hf < NHALF; ++hf) {
+      s[hf] = f32x16{};
+      dp[hf] = negD16;
     }
-    // register r holds tile key 16 (r / 8) + 8 g + r % 8; hide keys past the segment end or the diagonal
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int hf = 0; hf < NHALF; ++hf) {
+        s[hf] = mfma(*(const bf16x8*)(kn + k_lane + 8192 * hf + 512 * ks), qf[ks], s[hf]);
+        dp[hf] = mfma(*(const bf16x8*)(vn + k_lane + 8192 * hf + 512 * ks), dof[ks], dp[hf]);
+      }
+    // register r of block hf holds tile key 32 hf + 16 (r / 8) + 8 g + r % 8; hide keys past the
+    // segment end or the diagonal
     const bool need_mask = (c.k0 + BNQ > c.kv_len) || (c.causal && c.k0 + BNQ - 1 > c.delta + p0);
     if (need_mask) {
       int lim = c.kv_len - 1 - c.k0;
@@ -229,22 +248,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       }
       lim = (lim < -1 ? -1 : (lim > 1000 ? 1000 : lim)) - 8 * g;
 #pragma unroll
+      for (int hf = 0; hf < NHALF; ++hf)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 32 * hf + 16 * (r >> 3) + (r & 7);
+          s[hf][r] = kk > lim ? -INFINITY : s[hf][r];
+        }
+    }
+    bf16x8 dsf[NHALF][2];  // dS^T as B operands: dsf[hf][st] holds keys 32 hf + 16 st + 8 g + 0..7
+#pragma unroll
+    for (int hf = 0; hf < NHALF; ++hf)
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kk = 16 * (r >> 3) + (r & 7);
-        s[r] = kk > lim ? -INFINITY : s[r];
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[hf][r], c2, w1c));
+        dsf[hf][r >> 3][r & 7] = (__bf16)(p * dp[hf][r]);
       }
-    }
-    bf16x8 dsf[2];  // dS^T as B operands: dsf[st] holds keys 16 st + 8 g + 0..7
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, w1c));
-      dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
-    }
+    for (int hf = 0; hf < NHALF; ++hf)
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int dvb = 0; dvb < 4; ++dvb)
-        acc[dvb] = mfma(tr_read(kt + v_lane[dvb] + 16 * st * ROWB), dsf[st], acc[dvb]);
+        for (int dvb = 0; dvb < 4; ++dvb)
+          acc[dvb] = mfma(tr_read(kt + v_lane[dvb] + (32 * hf + 16 * st) * ROWB), dsf[hf][st], acc[dvb]);
   };
 
   // double buffer: tile n in buffer n % 2; tile n + 1 is staged while tile n is computed
