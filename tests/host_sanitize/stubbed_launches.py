@@ -103,6 +103,11 @@ def test_step_chunk_and_row_kernels():
     assert ra._lib.ra_merge(ctypes.byref(a), P, P, P, P, P, P, None) == ra.RA_OK
     assert ra._lib.ra_permute(2, 1, 1, 8, 1 << 20, 32, 128, ra.RA_BF16, P, P + (1 << 30), None) == ra.RA_OK
     assert LAST.value == 8 << 20
+    # [B, S, H, d] source read through strides, into a chunk-major destination
+    S, H, d = 1 << 20, 8, 128
+    assert ra._lib.ra_permute_strided(2, 1, 1, H, S, 32, d, ra.RA_BF16, P, S * H * d, d, H * d,
+                                      P + (1 << 30), H * S * d, S * d, d, None) == ra.RA_OK
+    assert LAST.value == H * S
     f = _desc("contiguous", 32, 4, 1, 1, causal=0, count=4, in_dtype=ra.RA_F32, d=16)
     assert ra._lib.ra_ring_fwd(ctypes.byref(f), P, P, P, P, P, None, 0, None) == ra.RA_OK
 
