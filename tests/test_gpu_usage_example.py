@@ -35,3 +35,8 @@ def test_usage_example():
     ref, ref_lse = OA.attention_reference(q[:, :, rows].cpu(), k.cpu(), v.cpu(), causal=True, q_pos=rows,
                                           k_pos=np.arange(S))
     assert max_abs(out_logical[:, :, rows], ref) <= TOL["bf16"]
+    # a [B, S, H, d] buffer read in place through a strided view
+    x_bshd = torch.randn(1, S, 8, 128, device="cuda").to(torch.bfloat16)
+    xp = api.to_chunked(x_bshd.transpose(1, 2), "zigzag", N)
+    torch.cuda.synchronize()
+    assert torch.equal(xp, api.to_chunked(x_bshd.transpose(1, 2).contiguous(), "zigzag", N))
