@@ -68,6 +68,30 @@ def _link(objs, lib, verbose):
     os.replace(tmp, lib)
 
 
+# a plain C (C99) caller of the library, run by the C-ABI test
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "ring_fwd_example.c")
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "ring_fwd_example")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the C-ABI example")
+    rel = os.path.relpath(PKG, os.path.dirname(C_EXAMPLE))
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+           "-isystem", os.path.join(rocm, "include"), "-I", INCLUDE, C_EXAMPLE_SRC, "-o", C_EXAMPLE + ".tmp",
+           "-L", PKG, "-lringattn", f"-Wl,-rpath,$ORIGIN/{rel}", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C example build failed:\n{res.stderr}")
+    os.replace(C_EXAMPLE + ".tmp", C_EXAMPLE)
+    return C_EXAMPLE
+
+
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = SOURCES + [PROBE_SRC]
@@ -75,6 +99,7 @@ def build_library(verbose: bool = False) -> str:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     _link(objs[:len(SOURCES)], LIB, verbose)
     _link(objs[len(SOURCES):], PROBE_LIB, verbose)
+    build_c_example(verbose)
     return LIB
 
 
