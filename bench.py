@@ -30,8 +30,10 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix and packed vector)
 # the sources the forward kernel is compiled from (the traffic record is keyed by their hash)
+# the forward kernel's sources and the build script that holds its compiler flags
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_long_context_amd", "csrc", f)
-                  for f in ("attn_fwd_bf16.hip", "fwd_common.h", "kernels.h", "schedule.h")]
+                  for f in ("attn_fwd_bf16.hip", "fwd_common.h", "kernels.h", "schedule.h")] + \
+                 [os.path.join(ROOT, "exact_long_context_amd", "build.py")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_zigzag_1m_gqa.json")
 TRAFFIC_WORKLOAD = "zigzag_1m_gqa"   # the workload the counter runs were taken on
 
