@@ -112,3 +112,27 @@ def test_ring_order_equals_definition(layout, causal, query_chunks):
     for j in range(N):
         assert np.max(np.abs(dks[j] - dk_ref[:, :, pos[j]])) <= 1e-12
         assert np.max(np.abs(dvs[j] - dv_ref[:, :, pos[j]])) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_matches_torch_autograd(causal):
+    """A library routine: torch's float64 scaled_dot_product_attention on the
+    CPU, differentiated by autograd, with grouped heads and the causal rule
+    written as a mask over arbitrary positions; every entry of dq, dk, dv."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    B, hq, hkv, Lq, Lk, d = 2, 4, 2, 33, 47, 16
+    q, k, v, do = _inputs(11, B, hq, hkv, Lq, Lk, d)
+    rng = np.random.default_rng(12)
+    q_pos = np.sort(rng.choice(np.arange(Lk), size=Lq, replace=False))
+    k_pos = np.arange(Lk)  # key 0 is visible to every query
+    kw = dict(causal=causal, q_pos=q_pos, k_pos=k_pos)
+    dq, dk, dv = BW.attention_backward_reference(q, k, v, do, **kw)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    mask = None
+    if causal:
+        mask = torch.tensor(k_pos[None, :] <= q_pos[:, None])
+    out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, enable_gqa=True)
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(got - want.numpy())) <= 1e-11
