@@ -15,10 +15,12 @@
 // Every product is a v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and
 // dS are rounded to bf16 as MFMA operands.
 //
-// Layouts in LDS (as in the forward kernel): "natural" tiles, where an
-// operand read takes 16 rows at one 16-byte chunk (k_pos: blocks of 16 rows,
-// the 16-byte chunks of the 16 rows side by side), and "transposing" tiles
-// for ds_read_b64_tr_b16 (v_pos: row-major, chunk c of row r at c ^ 4 (r % 4)).
+// Layouts in LDS: blocks of 16 rows, the 16-byte chunks of the 16 rows side
+// by side (k_pos), so that an operand read takes 16 rows at one chunk; the
+// per-step tiles also swap the rows inside a block by chunk (sw_pos: chunk c
+// of row r at slot (r % 16) ^ 4 (c % 4)), so that one copy serves both the
+// plain operand reads and the transposing ds_read_b64_tr_b16 reads (4 rows
+// at 4 neighbouring chunk halves per 16 lanes) without bank conflicts.
 // Tiles are filled by buffer loads that write LDS directly; rows past the end
 // of their segment arrive as zeros.
 #include <hip/hip_runtime.h>
@@ -57,10 +59,10 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
 __device__ __forceinline__ uint32_t nat_src(int blk, int lane, uint32_t rs) {
   return (uint32_t)(16 * (blk >> 2) + (lane & 15)) * rs + (uint32_t)(4 * (blk & 3) + (lane >> 4)) * 16;
 }
-// transposing tile: block blk = rows 4 blk .. 4 blk + 3; the lane landing on stored chunk lane % 16 of
-// row r fetches chunk (lane % 16) ^ 4 (r % 4), with r % 4 = lane / 16
-__device__ __forceinline__ uint32_t tr_src(int blk, int lane, uint32_t rs) {
-  return (uint32_t)(4 * blk + (lane >> 4)) * rs + (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) << 4);
+// swizzled tile: the same blocks; the lane landing on slot lane % 16 of chunk c = 4 (blk % 4) + lane / 16
+// fetches row (lane % 16) ^ 4 (c % 4) of the block, with c % 4 = lane / 16
+__device__ __forceinline__ uint32_t sw_src(int blk, int lane, uint32_t rs) {
+  return (uint32_t)(16 * (blk >> 2) + ((lane & 15) ^ ((lane >> 4) << 2))) * rs + (uint32_t)(4 * (blk & 3) + (lane >> 4)) * 16;
 }
 
 // One 16-byte-per-lane buffer load that writes LDS directly (lane l to byte 16 l of a 1 KiB block
@@ -79,21 +81,29 @@ __device__ __forceinline__ void dma_untracked(const void* base, uint32_t nrec, u
 }
 #pragma clang diagnostic pop
 
-// Two transposing reads: lane 16 G + j gets rows 4 t .. 4 t + 3 of column c0 + 16 (G % 2) + j for the
-// first and rows + 4 for the second (see v_lane below), i.e. an MFMA A operand with 8 consecutive rows
-// along k.
-__device__ __forceinline__ bf16x8 tr_read(const unsigned char* p) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
+// Two transposing reads from a swizzled tile: lane 16 G + j gets rows 8 g .. 8 g + 3 (from lo) and
+// 8 g + 4 .. 8 g + 7 (from hi) of column 32 dvb + 16 (G % 2) + j, i.e. an MFMA A operand (rows d,
+// k = the tile's rows) with 8 consecutive rows along k; lo and hi come from tr_lane.
+__device__ __forceinline__ bf16x8 tr_read(const unsigned char* lo_p, const unsigned char* hi_p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo_p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi_p);
   const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Per-lane offset of the transposing operand of dv/d block dvb inside a v_pos tile: A operand rows
-// (dv or d) 32 dvb + l32, k (keys or queries) 8 g + 0..7; add 16 st rows for the 16-step st.
-__device__ __forceinline__ int v_lane_of(int lane, int dvb) {
-  const int G = lane >> 4, j = lane & 15, q = j >> 2, g = lane >> 5;
-  return (8 * g + q) * ROWB + ((((dvb ^ q) << 2) + 2 * (G & 1) + ((j & 3) >> 1)) << 4) + (j & 1) * 8;
+// Per-lane offset inside a swizzled tile of the transposing reads for d block 0 and rows 0..15
+// (add 1024 dvb for d block dvb, 4096 for each further 16 rows): the lane supplies 4 columns
+// 32 dvb + 16 (G % 2) + 4 (j % 4) .. + 3 of row 8 g + j / 4 (+ 4 for hi), from chunk
+// 4 dvb + 2 (G % 2) + (j % 4) / 2, half j % 2.
+__device__ __forceinline__ int tr_lane(int lane, int hi) {
+  const int G = lane >> 4, j = lane & 15, g = lane >> 5;
+  const int c3 = 2 * (G & 1) + ((j & 3) >> 1);
+  return 256 * c3 + (((8 * g + (j >> 2) + 4 * hi) ^ (c3 << 2)) << 4) + 8 * (j & 1);
+}
+// Per-lane offset inside a swizzled tile of the plain operand read of row `row` (of the first 16-row
+// block pair addressed by the caller) at chunk 2 ks + g, for ks of parity p (add 512 ks).
+__device__ __forceinline__ int nat_lane(int row, int g, int p) {
+  return (row >> 4) * 4096 + g * 256 + (((row & 15) ^ (8 * p + 4 * g)) << 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -141,12 +151,13 @@ constexpr int QTILE = BNQ * ROWB;    // bytes of one tile kind
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
-  // Two buffers, each of K natural (S^T = K Q^T), K transposing (dQ^T += K^T dS^T) and V natural
-  // (dP^T = V dO^T), in one array: buffer B of tile kind T at (3 B + T) QTILE.  The loop body is one
-  // tile with the buffer index a loop variable (two unrolled bodies made the compiler copy the dQ
-  // accumulators between register sets on every tile); the loads are written out (dma_untracked)
-  // and waited for explicitly, so the compiler adds no waits for them before the operand reads.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[6 * QTILE];
+  // Two buffers, each of K (read plainly for S^T = K Q^T and transposed for dQ^T += K^T dS^T) and V
+  // (dP^T = V dO^T), swizzled tiles in one array: buffer B of tile kind T at (2 B + T) QTILE.  The
+  // loop body is one tile with the buffer index a loop variable (two unrolled bodies made the
+  // compiler copy the dQ accumulators between register sets on every tile); the loads are written
+  // out (dma_untracked) and waited for explicitly, so the compiler adds no waits for them before the
+  // operand reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * QTILE];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -186,20 +197,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const unsigned char* Kg = (const unsigned char*)f.k + ((int64_t)it.b * f.k_sb + (int64_t)it.kvh * f.k_sh) * 2;
   const unsigned char* Vg = (const unsigned char*)f.v + ((int64_t)it.b * f.v_sb + (int64_t)it.kvh * f.v_sh) * 2;
   const uint32_t kss = (uint32_t)(f.k_ss * 2), vss = (uint32_t)(f.v_ss * 2);
-  // DMA: wave w moves blocks w + 8 i (i < NHALF) of each of the three tiles
-  uint32_t kn_src[NHALF], kt_src[NHALF], vn_src[NHALF];
+  // DMA: wave w moves blocks w + 8 i (i < NHALF) of each of the two tiles
+  uint32_t kn_src[NHALF], vn_src[NHALF];
 #pragma unroll
   for (int i = 0; i < NHALF; ++i) {
-    kn_src[i] = nat_src(wave + 8 * i, lane, kss);
-    kt_src[i] = tr_src(wave + 8 * i, lane, kss);
-    vn_src[i] = nat_src(wave + 8 * i, lane, vss);
+    kn_src[i] = sw_src(wave + 8 * i, lane, kss);
+    vn_src[i] = sw_src(wave + 8 * i, lane, vss);
   }
   const int blk_dst = __builtin_amdgcn_readfirstlane(wave * 1024);
 
-  const int k_lane = k_pos(kperm(l32), g);  // natural operand, 16-d step ks: + 512 ks
-  int v_lane[4];
-#pragma unroll
-  for (int dvb = 0; dvb < 4; ++dvb) v_lane[dvb] = v_lane_of(lane, dvb);
+  // plain operand reads (keys permuted), 16-d step ks: + 512 ks from the base of its parity
+  const int k_lane0 = nat_lane(kperm(l32), g, 0), k_lane1 = nat_lane(kperm(l32), g, 1);
+  const int t_lo = tr_lane(lane, 0), t_hi = tr_lane(lane, 1);  // transposing reads of K
 
   f32x16 acc[4];  // dQ^T[d = 32 dvb + 8 (r / 4) + 4 g + r % 4][query my_p]
 #pragma unroll
@@ -211,19 +220,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     const uint32_t nk = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * kss + ROWB;
     const uint32_t nv = c.done ? 0u : (uint32_t)(c.kv_row + c.kv_len - 1) * vss + ROWB;
     const uint32_t sk = (uint32_t)(c.kv_row + c.k0) * kss, sv = (uint32_t)(c.kv_row + c.k0) * vss;
-    const uint32_t base = lds0 + (uint32_t)(3 * B * QTILE + blk_dst);
+    const uint32_t base = lds0 + (uint32_t)(2 * B * QTILE + blk_dst);
 #pragma unroll
     for (int i = 0; i < NHALF; ++i) {
       dma_untracked(Kg, nk, base + 8192 * i, kn_src[i], sk);
-      dma_untracked(Kg, nk, base + QTILE + 8192 * i, kt_src[i], sk);
-      dma_untracked(Vg, nv, base + 2 * QTILE + 8192 * i, vn_src[i], sv);
+      dma_untracked(Vg, nv, base + QTILE + 8192 * i, vn_src[i], sv);
     }
   };
 
   auto compute = [&](const TileCursor<BNQ>& c, int B) __attribute__((always_inline)) {
-    const unsigned char* kn = smem + 3 * B * QTILE;
-    const unsigned char* kt = kn + QTILE;
-    const unsigned char* vn = kn + 2 * QTILE;
+    const unsigned char* kn = smem + 2 * B * QTILE;
+    const unsigned char* vn = kn + QTILE;
     f32x16 s[NHALF], dp[NHALF];  // block hf: tile keys 32 hf ..; dp: dP^T - D
 #pragma unroll
     for (int hf = 0; hf < NHALF; ++hf) {
@@ -234,8 +241,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int hf = 0; hf < NHALF; ++hf) {
-        s[hf] = mfma(*(const bf16x8*)(kn + k_lane + 8192 * hf + 512 * ks), qf[ks], s[hf]);
-        dp[hf] = mfma(*(const bf16x8*)(vn + k_lane + 8192 * hf + 512 * ks), dof[ks], dp[hf]);
+        const int kl = (ks & 1) ? k_lane1 : k_lane0;
+        s[hf] = mfma(*(const bf16x8*)(kn + kl + 8192 * hf + 512 * ks), qf[ks], s[hf]);
+        dp[hf] = mfma(*(const bf16x8*)(vn + kl + 8192 * hf + 512 * ks), dof[ks], dp[hf]);
       }
     // register r of block hf holds tile key 32 hf + 16 (r / 8) + 8 g + r % 8; hide keys past the
     // segment end or the diagonal
@@ -268,8 +276,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int dvb = 0; dvb < 4; ++dvb)
-          acc[dvb] = mfma(tr_read(kt + v_lane[dvb] + (32 * hf + 16 * st) * ROWB), dsf[hf][st], acc[dvb]);
+        for (int dvb = 0; dvb < 4; ++dvb) {
+          const unsigned char* kt = kn + 1024 * dvb + 4096 * (st + 2 * hf);
+          acc[dvb] = mfma(tr_read(kt + t_lo, kt + t_hi), dsf[hf][st], acc[dvb]);
+        }
   };
 
   // double buffer: tile n in buffer n % 2; tile n + 1 is staged while tile n is computed
@@ -318,13 +328,14 @@ struct StepCursor {
 
 __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const FwdArgs& f = a.f;
-  // One LDS array with explicit offsets.  The per-step tiles (two buffers each of Q natural for
-  // S = Q K^T, Q transposing for dK^T += Q^T dS, dO natural for dP = dO V^T, dO transposing for
-  // dV^T += dO^T P) sit in the first 64 KiB, where every operand address is one register plus an
-  // instruction offset; V of the workgroup's 256 keys (natural layout, for the whole launch) and the
-  // per-row terms follow.  The step loads are written out (dma_untracked) and waited for explicitly.
-  constexpr int QN = 0, QT = 2 * TILE32, ON = 4 * TILE32, OT = 6 * TILE32;  // + B * TILE32
-  constexpr int VS = 8 * TILE32;                 // 64 KiB
+  // One LDS array with explicit offsets.  The per-step tiles (two buffers each of Q, read plainly
+  // for S = Q K^T and transposed for dK^T += Q^T dS, and of dO, read plainly for dP = dO V^T and
+  // transposed for dV^T += dO^T P; swizzled tiles) sit in the first 32 KiB, where every operand
+  // address is one register plus an instruction offset; V of the workgroup's 256 keys (k_pos
+  // layout, for the whole launch) and the per-row terms follow.  The step loads are written out
+  // (dma_untracked) and waited for explicitly.
+  constexpr int QN = 0, ON = 2 * TILE32;         // + B * TILE32
+  constexpr int VS = 4 * TILE32;                 // 32 KiB
   constexpr int WT = VS + KV_TILE * ROWB;        // + B * 256: -lse / scale, then -D, of the step's rows
   __shared__ __attribute__((aligned(1024))) unsigned char smem[WT + 512];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
@@ -390,15 +401,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const float c2 = f.scale_log2;
   const int64_t rows_total = (int64_t)f.batch * f.hq * a.q_rows;
   const uint32_t w_bytes = (uint32_t)(2 * rows_total * 4);
-  const int q_lane = k_pos(kperm(l32), g);        // natural operand (query rows permuted): + 512 ks
+  // plain operand reads (query rows permuted), 16-d step ks: + 512 ks from the base of its parity
+  const int q_lane0 = nat_lane(kperm(l32), g, 0), q_lane1 = nat_lane(kperm(l32), g, 1);
   // V as B operand (lane = key): + 512 s; the per-row terms of the step (lanes read 8 g ..)
   const unsigned char* vb_addr = smem + VS + k_pos(32 * wave + l32, g);
   const unsigned char* w_lane = smem + WT;
-  int t_lane[4];
-#pragma unroll
-  for (int dvb = 0; dvb < 4; ++dvb) t_lane[dvb] = v_lane_of(lane, dvb);
-  const uint32_t qn_src = nat_src(wave, lane, qss), qt_src = tr_src(wave, lane, qss);
-  const uint32_t on_src = nat_src(wave, lane, oss), ot_src = tr_src(wave, lane, oss);
+  const int t_lo = tr_lane(lane, 0), t_hi = tr_lane(lane, 1);  // transposing reads of Q and dO
+  const uint32_t qn_src = sw_src(wave, lane, qss), on_src = sw_src(wave, lane, oss);
   const int blk_dst = __builtin_amdgcn_readfirstlane(wave * 1024);
 
   f32x16 acck[4], accv[4];  // dK^T / dV^T[d = 32 dvb + 8 (r / 4) + 4 g + r % 4][key my_k]
@@ -461,9 +470,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     const uint32_t nq = (uint32_t)end * qss + ROWB, no = (uint32_t)end * oss + ROWB;
     const uint32_t sq = (uint32_t)(c.q_row0 + c.p0) * qss, so = (uint32_t)(c.q_row0 + c.p0) * oss;
     dma_untracked(Qg, nq, lds0 + QN + B * TILE32 + blk_dst, qn_src, sq);
-    dma_untracked(Qg, nq, lds0 + QT + B * TILE32 + blk_dst, qt_src, sq);
     dma_untracked(Og, no, lds0 + ON + B * TILE32 + blk_dst, on_src, so);
-    dma_untracked(Og, no, lds0 + OT + B * TILE32 + blk_dst, ot_src, so);
     if (wave == 0 && lane < 16) {
       // lanes 0..7: -lse / scale of the 32 rows; lanes 8..15: -D
       const uint32_t row = (uint32_t)(((int64_t)b * f.hq + h) * a.q_rows + c.q_row0 + c.p0);
@@ -475,9 +482,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   auto compute = [&](const StepCursor& c, auto bc) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
     const unsigned char* qn = smem + QN + B * TILE32;
-    const unsigned char* qt = smem + QT + B * TILE32;
     const unsigned char* on = smem + ON + B * TILE32;
-    const unsigned char* ot = smem + OT + B * TILE32;
     const float* wt = (const float*)(w_lane + B * 256);
     // register r of lane (key l32, g) holds query row 16 (r / 8) + 8 g + r % 8 of the step
     f32x16 s, dp;
@@ -495,8 +500,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     // S + (-lse / scale) and dP + (-D)
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = mfma(*(const bf16x8*)(qn + q_lane + 512 * ks), kf[ks], s);
-      dp = mfma(*(const bf16x8*)(on + q_lane + 512 * ks), *(const bf16x8*)(vb_addr + 512 * ks), dp);
+      const int ql = (ks & 1) ? q_lane1 : q_lane0;
+      s = mfma(*(const bf16x8*)(qn + ql + 512 * ks), kf[ks], s);
+      dp = mfma(*(const bf16x8*)(on + ql + 512 * ks), *(const bf16x8*)(vb_addr + 512 * ks), dp);
     }
     // hide rows past the segment end and pairs past the diagonal
     const bool need_mask = (c.p0 + BQ > c.qlen) || (c.causal && kw0 + 31 - c.p0 > c.delta);
@@ -520,8 +526,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int dvb = 0; dvb < 4; ++dvb) {
-        accv[dvb] = mfma(tr_read(ot + t_lane[dvb] + 16 * st * ROWB), pb[st], accv[dvb]);
-        acck[dvb] = mfma(tr_read(qt + t_lane[dvb] + 16 * st * ROWB), db[st], acck[dvb]);
+        const int o = 1024 * dvb + 4096 * st;
+        accv[dvb] = mfma(tr_read(on + o + t_lo, on + o + t_hi), pb[st], accv[dvb]);
+        acck[dvb] = mfma(tr_read(qn + o + t_lo, qn + o + t_hi), db[st], acck[dvb]);
       }
   };
 
