@@ -55,7 +55,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
 }
 
 // Per-lane byte offsets for the DMA of one 1 KiB block.
-// natural tile: block blk (0..7 for 32 rows) = rows 16 (blk / 4) .. + 15, chunks 4 (blk % 4) .. + 3
+// k_pos tile: block blk (0..7 for 32 rows) = rows 16 (blk / 4) .. + 15, chunks 4 (blk % 4) .. + 3
 __device__ __forceinline__ uint32_t nat_src(int blk, int lane, uint32_t rs) {
   return (uint32_t)(16 * (blk >> 2) + (lane & 15)) * rs + (uint32_t)(4 * (blk & 3) + (lane >> 4)) * 16;
 }
