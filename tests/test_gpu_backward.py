@@ -161,3 +161,37 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(*runs):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def _bshd(x: torch.Tensor, dtype=None) -> torch.Tensor:
+    """A [B, S, H, d] buffer seen as [B, H, S, d] (row stride H d elements),
+    holding x's values (or uninitialised, in dtype, when dtype is given)."""
+    B, H, S, d = x.shape
+    buf = torch.empty(B, S, H, d, dtype=dtype or x.dtype, device=x.device).transpose(1, 2)
+    if dtype is None:
+        buf.copy_(x)
+    return buf
+
+
+def test_backward_strided_views_bitwise():
+    """ra_ring_bwd reading q, k, v, out and dout in place from [B, S, H, d]
+    buffers (every staged row at a row stride of H d elements, not d) and
+    writing the gradients with the same strides: bit for bit the gradients of
+    the contiguous call, since no arithmetic depends on the strides."""
+    print("case bwd strided views", flush=True)
+    w = synthetic.Workload("t", 1, 8, 2, 1600, 8, 128, "bf16", True, "zigzag", seed=67)
+    qp, kp, vp, k, v, do = _setup(w, seed_do=69)
+    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=True)
+    want = api.ring_backward(qp, kp, vp, out, do, lse, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout,
+                             causal=True)
+    qs, ks, vs, outs, dos = (_bshd(t) for t in (qp, kp, vp, out, do))
+    assert qs.stride(2) == w.hq * w.d and ks.stride(2) == w.hkv * w.d
+    got = tuple(_bshd(t, torch.float32) for t in (qp, kp, vp))
+    desc = ra.ring_desc(qs, ks, vs, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=True, out=outs,
+                        lse=lse)
+    need = ra.ra_ring_bwd_workspace_bytes(desc)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    ra.ra_ring_bwd(desc, qs, ks, vs, outs, dos, lse, *got, ws, need)
+    torch.cuda.synchronize()
+    for a, b in zip(got, want):
+        assert torch.equal(a.contiguous().view(torch.int32), b.view(torch.int32))
