@@ -1,11 +1,13 @@
 """The usage example of the README, run as written (device tensors in logical
-token order, the chunk-major permutation, forward, backward, and back), with
-its results checked against the oracle on a few rows."""
+token order, the chunk-major permutation, forward, backward, and back, a
+strided view, and one query chunk step by step as one device of a ring runs
+it), with its results checked against the oracle on a few rows."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import attention as OA
+from oracle import layout as OL
 
 from .parity_utils import TOL, max_abs
 
@@ -40,3 +42,22 @@ def test_usage_example():
     xp = api.to_chunked(x_bshd.transpose(1, 2), "zigzag", N)
     torch.cuda.synchronize()
     assert torch.equal(xp, api.to_chunked(x_bshd.transpose(1, 2).contiguous(), "zigzag", N))
+    # one device of a ring (ra_ring_step): query chunk i stays, KV chunks arrive in ring order
+    i, L = 2, S // N
+    qi = qp[:, :, i * L:(i + 1) * L]
+    st = api.state_init(qi, kp)
+    for t in range(N):
+        j = (i - t) % N                                   # the KV chunk held at step t
+        api.ring_step(st, qi, kp[:, :, j * L:(j + 1) * L], vp[:, :, j * L:(j + 1) * L],
+                      step=t, seq=S, n_chunks=N, layout="zigzag", causal=True, q_chunk=i)
+    out_i, lse_i = api.finalize(st, qi)                   # chunk i of out and lse
+    torch.cuda.synchronize()
+    # the same chunk from the fused launch, and a few of its rows against the definition
+    assert max_abs(out_i, out[:, :, i * L:(i + 1) * L]) <= TOL["bf16"]
+    assert max_abs(lse_i, lse[:, :, i * L:(i + 1) * L]) <= TOL["bf16"]
+    pos_i = OL.chunk_positions("zigzag", S, N, i)
+    sel = np.array([0, 1, L // 2 - 1, L // 2, L - 1])
+    ref_i, ref_lse_i = OA.attention_reference(qi[:, :, sel].cpu(), k.cpu(), v.cpu(), causal=True,
+                                              q_pos=pos_i[sel], k_pos=np.arange(S))
+    assert max_abs(out_i[:, :, sel], ref_i) <= TOL["bf16"]
+    assert max_abs(lse_i[:, :, sel], ref_lse_i) <= TOL["bf16"]
