@@ -111,10 +111,12 @@ def test_full_backward_zigzag_1m_sampled():
     bench times (the library's forward output and lse as inputs): dq on 512
     seeded query rows against the oracle (each row against all its visible
     keys; a dq row needs only its own row's scores); dk and dv, whose rows
-    depend on every query row of the chunk, through the sums over the keys of
-    each KV head that hold at any size (key gradients cancel; value gradients
-    add up to the upstream gradients within the bf16 rounding of the
-    weights), and finite everywhere."""
+    depend on up to every query row of the chunk, element by element on the
+    last 32 keys of every KV head (seen by only the chunk's last 32 rows) and,
+    for all keys, through the sums over the keys of each KV head that hold at
+    any size (key gradients cancel; value gradients add up to the upstream
+    gradients within the bf16 rounding of the weights), and finite
+    everywhere."""
     from oracle import backward as OB
     from .parity_utils import query_rows_positions, run_threaded
     w = synthetic.WORKLOADS["zigzag_1m_gqa"]
@@ -159,6 +161,38 @@ def test_full_backward_zigzag_1m_sampled():
     err = max_abs(dq[0, hs, rs].cpu().double().numpy(), want)
     print(f"  dq max-abs error on {len(samples)} rows {err:.2e} (magnitude {np.abs(want).max():.2e})", flush=True)
     assert err <= TOL["bf16"]
+
+    # dk and dv of the last M keys of the sequence, the end of the query chunk's
+    # own late segment: of all query rows of the chunk only its last M rows see
+    # them, so the oracle's ring-order backward over those rows (given their
+    # out and lse over all their visible keys) yields these key rows exactly
+    from oracle import attention as OA
+    from oracle import layout as OL
+    M = 32
+    tail = np.arange(w.chunk - M, w.chunk)                # buffer rows of query chunk 0 and KV chunk 0
+    tpos = OL.chunk_positions(w.layout, w.seq, w.n_chunks, 0)[tail]
+    assert (tpos == np.arange(w.seq - M, w.seq)).all()
+
+    def tail_grads(g):
+        hs_ = list(range(g * G, (g + 1) * G))
+        qs, dos = qc[:, hs_][:, :, tail], doc[:, hs_][:, :, tail]
+        o_ref, lse_ref = OA.attention_reference(qs, kc[:, g:g + 1], vc[:, g:g + 1], causal=True, q_pos=tpos,
+                                                k_pos=np.arange(w.seq))
+        _, dks, dvs = OB.ring_attention_backward([qs], [kc[:, g:g + 1, w.seq - M:]], [vc[:, g:g + 1, w.seq - M:]],
+                                                 [dos], [o_ref], [lse_ref], {0: tpos}, query_chunks=[0],
+                                                 causal=True)
+        return g, dks[0][0, 0], dvs[0][0, 0]
+
+    for name, lib, pick in (("dk", dk, 1), ("dv", dv, 2)):
+        ref = np.stack([r[pick] for r in sorted(run_threaded(tail_grads, range(w.hkv)))])  # [Hkv, M, d]
+        got = lib[0, :, w.chunk - M:w.chunk].cpu().double().numpy()
+        err, mag = max_abs(got, ref), float(np.abs(ref).max())
+        print(f"  {name} on the last {M} keys of every KV head: max-abs error {err:.2e} (magnitude {mag:.2e})",
+              flush=True)
+        # every row that sees these keys spreads its weight over 1M keys, so their gradients are far
+        # below the absolute budget; P and dS are rounded to bf16 (relative 2^-9 per term), which
+        # bounds the error relative to the largest entry well under 2^-6
+        assert err <= 2.0 ** -6 * mag
 
 
 @pytest.mark.parametrize("name,qc", [("mha_8k", 0), ("causal_striped_128k", 15)])
