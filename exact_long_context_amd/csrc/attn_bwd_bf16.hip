@@ -100,8 +100,8 @@ __device__ __forceinline__ int tr_lane(int lane, int hi) {
   const int c3 = 2 * (G & 1) + ((j & 3) >> 1);
   return 256 * c3 + (((8 * g + (j >> 2) + 4 * hi) ^ (c3 << 2)) << 4) + 8 * (j & 1);
 }
-// Per-lane offset inside a swizzled tile of the plain operand read of row `row` (of the first 16-row
-// block pair addressed by the caller) at chunk 2 ks + g, for ks of parity p (add 512 ks).
+// Per-lane offset inside a swizzled tile of the plain operand read of tile row `row` (0..31; a
+// further 32 rows add 8192) at chunk 2 ks + g, for a 16-d step ks of parity p (add 512 ks).
 __device__ __forceinline__ int nat_lane(int row, int g, int p) {
   return (row >> 4) * 4096 + g * 256 + (((row & 15) ^ (8 * p + 4 * g)) << 4);
 }
