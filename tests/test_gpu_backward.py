@@ -173,21 +173,24 @@ def _bshd(x: torch.Tensor, dtype=None) -> torch.Tensor:
     return buf
 
 
-def test_backward_strided_views_bitwise():
+@pytest.mark.parametrize("batch,hq,hkv,S,N,layout,causal", [(1, 8, 2, 1600, 8, "zigzag", True),
+                                                            (2, 3, 3, 1152, 4, "striped", True),
+                                                            (2, 4, 1, 1000, 4, "contiguous", False)])
+def test_backward_strided_views_bitwise(batch, hq, hkv, S, N, layout, causal):
     """ra_ring_bwd reading q, k, v, out and dout in place from [B, S, H, d]
     buffers (every staged row at a row stride of H d elements, not d) and
     writing the gradients with the same strides: bit for bit the gradients of
     the contiguous call, since no arithmetic depends on the strides."""
-    print("case bwd strided views", flush=True)
-    w = synthetic.Workload("t", 1, 8, 2, 1600, 8, 128, "bf16", True, "zigzag", seed=67)
+    print(f"case bwd strided views B={batch} hq={hq} hkv={hkv} S={S} N={N} {layout} causal={causal}", flush=True)
+    w = synthetic.Workload("t", batch, hq, hkv, S, N, 128, "bf16", causal, layout, seed=67)
     qp, kp, vp, k, v, do = _setup(w, seed_do=69)
-    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=True)
+    out, lse = api.ring_forward(qp, kp, vp, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=causal)
     want = api.ring_backward(qp, kp, vp, out, do, lse, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout,
-                             causal=True)
+                             causal=causal)
     qs, ks, vs, outs, dos = (_bshd(t) for t in (qp, kp, vp, out, do))
     assert qs.stride(2) == w.hq * w.d and ks.stride(2) == w.hkv * w.d
     got = tuple(_bshd(t, torch.float32) for t in (qp, kp, vp))
-    desc = ra.ring_desc(qs, ks, vs, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=True, out=outs,
+    desc = ra.ring_desc(qs, ks, vs, seq=w.seq, n_chunks=w.n_chunks, layout=w.layout, causal=causal, out=outs,
                         lse=lse)
     need = ra.ra_ring_bwd_workspace_bytes(desc)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
