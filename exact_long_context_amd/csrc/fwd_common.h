@@ -26,13 +26,22 @@ struct WorkItem {
 // whole chip instead (XCD w % 8 serves stream w % S of the current group),
 // one group after another: the K / V of the streams in flight then stays
 // within the memory-side cache, where walking all streams at once would not.
+// With xcd_swizzle = 3 (streams that do not split over the XCDs, a multiple of
+// 256 workgroups) XCD w % 8 takes blocks of 32 consecutive workgroups of the
+// heaviest-first order, block b on XCD b % 8: the 32 workgroups an XCD runs at
+// a time are neighbouring tiles that walk the same keys in step, and the
+// blocks of every weight spread over all XCDs.
 // The KV ranges of one query tile (split-KV) take consecutive ranks.
 __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a, int32_t w) {
   const int32_t G = a.hq / a.hkv;
   const int32_t hg_count = G / a.heads_per_wg;
   const int32_t n_streams = a.batch * a.hkv;
   int32_t r, stream, hg;
-  if (a.xcd_swizzle > 1) {
+  if (a.xcd_swizzle == 3) {
+    const int32_t x = w & 7, u = w >> 3;
+    w = (((u >> 5) << 3) + x) * 32 + (u & 31);
+  }
+  if (a.xcd_swizzle == 2 || a.xcd_swizzle == 4) {
     const int32_t S = a.xcd_swizzle;
     const int32_t per_s = a.n_work / n_streams;  // workgroups per stream
     const int32_t grp = w / (S * per_s);
@@ -41,7 +50,7 @@ __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a, int32_t w) {
     const int32_t v = rem / S;
     r = v / hg_count;
     hg = v - r * hg_count;
-  } else if (a.xcd_swizzle) {
+  } else if (a.xcd_swizzle == 1) {
     const int32_t x = w & 7, u = w >> 3;
     const int32_t per = (n_streams >> 3) * hg_count;
     r = u / per;

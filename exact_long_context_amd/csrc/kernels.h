@@ -56,7 +56,8 @@ struct FwdArgs {
   int32_t rows_per_wg;    // query rows of one segment handled by one workgroup
   int32_t nseg_q;         // query segments per query chunk (2 for zig-zag)
   int32_t tiles_per_seg;  // workgroups along one query segment
-  int32_t xcd_swizzle;    // 1: one KV stream per XCD; 2 or 4: streams that many at a time over all XCDs
+  int32_t xcd_swizzle;    // 1: one KV stream per XCD; 2 or 4: streams that many at a time over all XCDs;
+                          // 3: blocks of 32 workgroups, block b on XCD b % 8
   int32_t n_work;         // total workgroups
   // split-KV (MODE_RING): each query tile's KV tiles, in ring order, are cut
   // into kv_splits consecutive ranges of (nearly) equal tile counts, one

@@ -142,6 +142,9 @@ ra_status plan_launch(ra::FwdArgs& a, bool bf16, int64_t seg_len, int32_t nseg_q
     const int64_t budget = (int64_t)128 << 20;
     if (streams * kv_stream > budget && 2 * kv_stream <= budget && 4 * kv_stream > budget) a.xcd_swizzle = 2;
   }
+  // Streams that do not split over the XCDs (one KV head, say): each XCD takes
+  // blocks of 32 neighbouring workgroups, which walk the same keys in step.
+  if (streams % 8 != 0 && total % 256 == 0) a.xcd_swizzle = 3;
   return RA_OK;
 }
 

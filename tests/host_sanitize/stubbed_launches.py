@@ -46,13 +46,15 @@ def _calls():
 
 # workgroup-to-XCD order: 1 = one KV stream per XCD (8 streams or a multiple),
 # 2 = the streams two at a time over all XCDs (two streams' K and V fit in
-# 128 MiB, all of them do not), 0 = no XCD order (streams not a multiple of 8)
+# 128 MiB, all of them do not), 3 = blocks of 32 neighbouring workgroups per
+# XCD (streams not a multiple of 8, workgroups a multiple of 256), 0 = none
 @pytest.mark.parametrize("name,args,work,xcd", [
     ("zigzag_1m_gqa", ("zigzag", 1 << 20, 32, 32, 8), 4096, 1),       # 8 streams x 2 segments x 256 tiles
     ("causal_contig_32k", ("contiguous", 1 << 15, 8, 32, 32, 1, 0, 8), 4096, 1),
     ("causal_striped_128k", ("striped", 1 << 17, 16, 8, 8, 1, 0, 16), 4096, 2),   # 8 streams of 64 MiB
     ("mha_8k", ("contiguous", 8192, 4, 8, 8, 0, 0, 4), 256, 1),
-    ("usp_1m_share", ("zigzag", 1 << 20, 4, 4, 1), 4096, 0),        # 1 stream x 2 segments x 2048 tiles
+    ("usp_1m_share", ("zigzag", 1 << 20, 4, 4, 1), 4096, 3),        # 1 stream x 2 segments x 2048 tiles
+    ("one stream, 4 x 16 tiles", ("contiguous", 4096, 4, 4, 1, 0, 0, 4), 64, 0),   # not a multiple of 256
 ])
 def test_ring_fwd_plans(name, args, work, xcd):
     r = _desc(*args)

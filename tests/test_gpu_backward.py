@@ -69,6 +69,7 @@ CASES = [
     ("striped", 1152, 4, 4, 2, True, None),         # L = 288: two 256-key tiles, the second ragged
     ("striped", 576, 8, 2, 2, False, (3,)),
     ("contiguous", 1000, 4, 2, 1, True, (2, 3)),    # L = 250
+    ("zigzag", 8192, 4, 8, 2, True, None),          # dQ: 256 workgroups over 2 KV streams, blocks of 32 per XCD
 ]
 
 

@@ -136,6 +136,7 @@ SMALL = [
     ("striped", 64, 64, 2, 1, 1, True),        # L = 1
     ("zigzag", 1024, 512, 2, 1, 1, True),      # 1024 KV segments: the largest run table
     ("contiguous", 1024, 1024, 2, 2, 1, True),  # 1024 chunks of one token
+    ("zigzag", 8192, 4, 8, 2, 1, True),        # 256 workgroups over 2 KV streams: blocks of 32 per XCD
 ]
 
 
